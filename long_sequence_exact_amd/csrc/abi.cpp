@@ -1,0 +1,488 @@
+// C ABI of libseqattn: argument validation, dispatch and launch on the
+// caller's stream.  Declarations, semantics and passages: include/seqattn.h.
+//
+// Every check runs before the first HIP call, so each error return can be
+// exercised on a machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/seqattn.h"
+#include "common.h"
+
+using namespace seqattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return SEQATTN_OK;
+}
+
+int esize(int32_t dt) { return dt == SEQATTN_BF16 ? 2 : 4; }
+
+bool dtype_valid(int32_t dt) { return dt == SEQATTN_BF16 || dt == SEQATTN_F32; }
+
+int64_t numel(const seqattn_tensor *t) { return t->b * t->h * t->n * t->d; }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+constexpr int64_t kMaxBH = (int64_t)1 << 20;
+
+// Structural checks of one descriptor: non-null, known dtype, non-negative
+// dims within range, non-negative strides, 16-byte row alignment (rows, d>1).
+int check_tensor(const seqattn_tensor *t, const char *name, bool is_lse)
+{
+    if (!t)
+        return fail(SEQATTN_ERR_NULL, "%s: descriptor is NULL", name);
+    if (!dtype_valid(t->dtype))
+        return fail(SEQATTN_ERR_DTYPE, "%s: unknown dtype %d", name, (int)t->dtype);
+    if (t->b < 0 || t->h < 0 || t->n < 0 || t->d < 0)
+        return fail(SEQATTN_ERR_SHAPE, "%s: negative dimension", name);
+    if (t->n >= kMaxRows || t->b * t->h >= kMaxBH || t->b >= kMaxBH || t->h >= kMaxBH)
+        return fail(SEQATTN_ERR_SHAPE, "%s: dimension too large", name);
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_n < 0)
+        return fail(SEQATTN_ERR_STRIDE, "%s: negative stride", name);
+    if (numel(t) > 0 && t->data == nullptr)
+        return fail(SEQATTN_ERR_NULL, "%s: data pointer is NULL", name);
+    if (is_lse) {
+        if (t->dtype != SEQATTN_F32)
+            return fail(SEQATTN_ERR_DTYPE, "%s: LSE must be fp32", name);
+        if (t->d != 1)
+            return fail(SEQATTN_ERR_SHAPE, "%s: LSE must have d == 1", name);
+        if (((uintptr_t)t->data) % 4)
+            return fail(SEQATTN_ERR_STRIDE, "%s: LSE data not 4-byte aligned", name);
+        return SEQATTN_OK;
+    }
+    const int es = esize(t->dtype);
+    if (numel(t) > 0) {
+        if (((uintptr_t)t->data) % 16)
+            return fail(SEQATTN_ERR_STRIDE, "%s: data not 16-byte aligned", name);
+        if ((t->b > 1 && (t->stride_b * es) % 16) || (t->h > 1 && (t->stride_h * es) % 16) ||
+            (t->n > 1 && (t->stride_n * es) % 16))
+            return fail(SEQATTN_ERR_STRIDE, "%s: strides must be multiples of 16 bytes", name);
+        if (t->n > 1 && t->stride_n < t->d)
+            return fail(SEQATTN_ERR_STRIDE, "%s: rows overlap (stride_n < d)", name);
+    }
+    return SEQATTN_OK;
+}
+
+// Byte range [lo, hi) spanned by a descriptor (empty tensor -> empty range).
+void extent(const seqattn_tensor *t, uintptr_t *lo, uintptr_t *hi)
+{
+    if (numel(t) == 0) {
+        *lo = *hi = 0;
+        return;
+    }
+    const int es = esize(t->dtype);
+    const int64_t last = (t->b - 1) * t->stride_b + (t->h - 1) * t->stride_h +
+                         (t->n - 1) * t->stride_n + t->d;
+    *lo = (uintptr_t)t->data;
+    *hi = (uintptr_t)t->data + (uintptr_t)last * es;
+}
+
+bool overlaps(const seqattn_tensor *a, const seqattn_tensor *b)
+{
+    uintptr_t al, ah, bl, bh;
+    extent(a, &al, &ah);
+    extent(b, &bl, &bh);
+    if (al == ah || bl == bh)
+        return false;
+    return al < bh && bl < ah;
+}
+
+View view_of(const seqattn_tensor *t)
+{
+    View v;
+    v.ptr = t->data;
+    v.sb = t->stride_b;
+    v.ss = 0;
+    v.sh = t->stride_h;
+    v.sn = t->stride_n;
+    return v;
+}
+
+float pick_scale(float s, int64_t d) { return s > 0.f ? s : 1.0f / sqrtf((float)d); }
+
+// Clamp delta into [-(Nq+1), Nk]; report non-causal when every key is visible
+// to every query (delta >= Nk - 1).
+void clamp_delta(int64_t delta, int64_t nq, int64_t nk, int *out, int *noncausal)
+{
+    if (delta == SEQATTN_NONCAUSAL || delta >= nk - 1) {
+        *noncausal = 1;
+        *out = (int)std::max<int64_t>(nk, 0);
+        return;
+    }
+    *noncausal = 0;
+    *out = (int)std::max<int64_t>(delta, -(nq + 1));
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(SEQATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared checks of (q, k, v) for the forward-style calls.
+int check_qkv(const seqattn_tensor *q, const seqattn_tensor *k, const seqattn_tensor *v,
+              bool same_len)
+{
+    int st;
+    if ((st = check_tensor(q, "q", false)) || (st = check_tensor(k, "k", false)) ||
+        (st = check_tensor(v, "v", false)))
+        return st;
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(SEQATTN_ERR_DTYPE, "q, k, v must share one dtype");
+    if (q->d != 64 && q->d != 128)
+        return fail(SEQATTN_ERR_SHAPE, "head dim d=%lld not supported (64 or 128)",
+                    (long long)q->d);
+    if (k->d != q->d || v->d != q->d)
+        return fail(SEQATTN_ERR_SHAPE, "q, k, v head dims differ");
+    if (k->b != q->b || v->b != q->b)
+        return fail(SEQATTN_ERR_SHAPE, "batch sizes differ");
+    if (v->h != k->h || v->n != k->n)
+        return fail(SEQATTN_ERR_SHAPE, "k and v shapes differ");
+    if (k->h == 0 || q->h % k->h != 0)
+        return fail(SEQATTN_ERR_SHAPE, "k->h (%lld) must divide q->h (%lld)",
+                    (long long)k->h, (long long)q->h);
+    if (same_len && k->n != q->n)
+        return fail(SEQATTN_ERR_SHAPE, "q and k/v lengths differ");
+    return SEQATTN_OK;
+}
+
+int check_out(const seqattn_tensor *o, const seqattn_tensor *lse, const seqattn_tensor *q,
+              const seqattn_tensor *k, const seqattn_tensor *v)
+{
+    int st;
+    if ((st = check_tensor(o, "o", false)) || (st = check_tensor(lse, "lse", true)))
+        return st;
+    if (o->b != q->b || o->h != q->h || o->n != q->n || o->d != q->d)
+        return fail(SEQATTN_ERR_SHAPE, "o must be [B, Hq, Nq, d] like q");
+    if (lse->b != q->b || lse->h != q->h || lse->n != q->n)
+        return fail(SEQATTN_ERR_SHAPE, "lse must be [B, Hq, Nq, 1]");
+    const seqattn_tensor *ins[3] = {q, k, v};
+    for (const seqattn_tensor *in : ins)
+        if (overlaps(o, in) || overlaps(lse, in))
+            return fail(SEQATTN_ERR_ALIAS, "outputs overlap an input");
+    if (overlaps(o, lse))
+        return fail(SEQATTN_ERR_ALIAS, "o and lse overlap");
+    return SEQATTN_OK;
+}
+
+hipStream_t stream_of(void *s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+int seqattn_version(void) { return SEQATTN_VERSION; }
+
+const char *seqattn_status_string(int status)
+{
+    switch (status) {
+    case SEQATTN_OK: return "ok";
+    case SEQATTN_ERR_NULL: return "null pointer";
+    case SEQATTN_ERR_DTYPE: return "unsupported or mismatched dtype";
+    case SEQATTN_ERR_SHAPE: return "invalid shape";
+    case SEQATTN_ERR_STRIDE: return "invalid stride or alignment";
+    case SEQATTN_ERR_ALIAS: return "output aliases an input";
+    case SEQATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SEQATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SEQATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *seqattn_last_error(void) { return g_err; }
+
+int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, int64_t causal_offset,
+                             float softmax_scale, uint32_t flags, seqattn_tensor *o,
+                             seqattn_tensor *lse, void *hip_stream)
+{
+    int st;
+    if ((st = check_qkv(q, k, v, false)) || (st = check_out(o, lse, q, k, v)))
+        return st;
+    if (flags & ~SEQATTN_ACCUMULATE)
+        return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const bool acc = flags & SEQATTN_ACCUMULATE;
+    if ((acc || q->dtype == SEQATTN_F32) && o->dtype != SEQATTN_F32)
+        return fail(SEQATTN_ERR_DTYPE, "o must be fp32 (accumulate or fp32 inputs)");
+
+    FwdParams p;
+    p.q = view_of(q);
+    p.k = view_of(k);
+    p.v = view_of(v);
+    p.o = view_of(o);
+    p.lse = view_of(lse);
+    p.B = (int)q->b;
+    p.S = 1;
+    p.Hq = (int)q->h;
+    p.Hkv = (int)k->h;
+    p.Nq = (int)q->n;
+    p.Nk = (int)k->n;
+    clamp_delta(causal_offset, q->n, k->n, &p.delta, &p.noncausal);
+    p.scale = pick_scale(softmax_scale, q->d);
+    p.accumulate = acc ? 1 : 0;
+    p.o_f32 = o->dtype == SEQATTN_F32;
+    if (p.Nq == 0 || p.B == 0 || p.Hq == 0)
+        return ok();
+    if (p.Nk == 0) {
+        if (acc)
+            return ok();
+        return hip_status(launch_fill_empty(p.o, p.lse, p.B, 1, p.Hq, p.Nq, (int)q->d,
+                                            p.o_f32, stream_of(hip_stream)),
+                          "fill_empty");
+    }
+    const hipError_t e = q->dtype == SEQATTN_BF16
+                             ? launch_fwd_bf16(p, (int)q->d, stream_of(hip_stream))
+                             : launch_fwd_f32(p, (int)q->d, stream_of(hip_stream));
+    return hip_status(e, "attn_segment_fwd launch");
+}
+
+int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
+                      const seqattn_tensor *o_b, const seqattn_tensor *lse_b,
+                      void *hip_stream)
+{
+    int st;
+    if ((st = check_tensor(o_acc, "o_acc", false)) ||
+        (st = check_tensor(lse_acc, "lse_acc", true)) ||
+        (st = check_tensor(o_b, "o_b", false)) || (st = check_tensor(lse_b, "lse_b", true)))
+        return st;
+    if (o_acc->dtype != SEQATTN_F32)
+        return fail(SEQATTN_ERR_DTYPE, "o_acc must be fp32");
+    if (o_acc->d % 4 != 0 || o_acc->d == 0)
+        return fail(SEQATTN_ERR_SHAPE, "d must be a positive multiple of 4");
+    if (o_b->b != o_acc->b || o_b->h != o_acc->h || o_b->n != o_acc->n || o_b->d != o_acc->d)
+        return fail(SEQATTN_ERR_SHAPE, "o_b shape differs from o_acc");
+    const seqattn_tensor *ls[2] = {lse_acc, lse_b};
+    for (const seqattn_tensor *l : ls)
+        if (l->b != o_acc->b || l->h != o_acc->h || l->n != o_acc->n)
+            return fail(SEQATTN_ERR_SHAPE, "lse shape must be [B, H, N, 1]");
+    if (overlaps(o_acc, o_b) || overlaps(o_acc, lse_b) || overlaps(lse_acc, o_b) ||
+        overlaps(lse_acc, lse_b) || overlaps(o_acc, lse_acc))
+        return fail(SEQATTN_ERR_ALIAS, "accumulator overlaps the merged partial");
+    MergeParams p;
+    p.oa = view_of(o_acc);
+    p.la = view_of(lse_acc);
+    p.ob = view_of(o_b);
+    p.lb = view_of(lse_b);
+    p.B = (int)o_acc->b;
+    p.H = (int)o_acc->h;
+    p.N = (int)o_acc->n;
+    p.d = (int)o_acc->d;
+    p.ob_f32 = o_b->dtype == SEQATTN_F32;
+    return hip_status(launch_lse_merge(p, stream_of(hip_stream)), "lse_merge launch");
+}
+
+size_t seqattn_workspace_size(int op, const seqattn_tensor *q, const seqattn_tensor *k,
+                              int32_t n_branches)
+{
+    (void)n_branches;
+    if (!q)
+        return 0;
+    switch (op) {
+    case SEQATTN_OP_DILATED_FWD:
+        // fp32 accumulator when the output o (passed as `k`) is bf16
+        if (k && k->dtype == SEQATTN_BF16)
+            return (size_t)(q->b * q->h * q->n * q->d) * sizeof(float);
+        return 0;
+    case SEQATTN_OP_SEGMENT_BWD:
+        // D_i = sum_c dO_ic O_ic per query row
+        return (size_t)(q->b * q->h * q->n) * sizeof(float);
+    default:
+        return 0;
+    }
+}
+
+int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, const int64_t *segment_lengths,
+                             const int64_t *dilations, int32_t n_branches,
+                             float softmax_scale, uint32_t flags, seqattn_tensor *o,
+                             seqattn_tensor *lse, void *workspace, size_t workspace_bytes,
+                             void *hip_stream)
+{
+    int st;
+    if ((st = check_qkv(q, k, v, true)) || (st = check_out(o, lse, q, k, v)))
+        return st;
+    if (q->dtype != SEQATTN_BF16)
+        return fail(SEQATTN_ERR_DTYPE, "dilated attention takes bf16 q/k/v");
+    if (!segment_lengths || !dilations)
+        return fail(SEQATTN_ERR_NULL, "segment_lengths / dilations are NULL");
+    if (n_branches < 1 || n_branches > 64)
+        return fail(SEQATTN_ERR_SHAPE, "n_branches must be in [1, 64]");
+    if (flags & ~SEQATTN_CAUSAL)
+        return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    for (int i = 0; i < n_branches; ++i)
+        if (segment_lengths[i] < 1 || dilations[i] < 1 || segment_lengths[i] >= kMaxRows ||
+            dilations[i] >= kMaxRows)
+            return fail(SEQATTN_ERR_SHAPE, "branch %d: w and r must be >= 1", i);
+    const bool o_bf16 = o->dtype == SEQATTN_BF16;
+    const size_t need = seqattn_workspace_size(SEQATTN_OP_DILATED_FWD, q, o, n_branches);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(SEQATTN_ERR_WORKSPACE, "need %zu bytes of workspace", need);
+        if ((uintptr_t)workspace % 16)
+            return fail(SEQATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    }
+    const int B = (int)q->b, Hq = (int)q->h, N = (int)q->n, d = (int)q->d;
+    if (B == 0 || Hq == 0 || N == 0)
+        return ok();
+    hipStream_t s = stream_of(hip_stream);
+
+    // The accumulator: o itself when fp32, else the fp32 workspace [B,Hq,N,d].
+    View acc = view_of(o);
+    if (o_bf16) {
+        acc.ptr = workspace;
+        acc.sb = (int64_t)Hq * N * d;
+        acc.sh = (int64_t)N * d;
+        acc.sn = d;
+    }
+    View lsev = view_of(lse);
+    const bool causal = flags & SEQATTN_CAUSAL;
+    const float scale = pick_scale(softmax_scale, d);
+
+    // A first branch with r = 1 selects every position: it can overwrite the
+    // accumulator instead of merging into an initialised one.
+    const bool first_writes = dilations[0] == 1;
+    if (!first_writes) {
+        hipError_t e = launch_fill_empty(acc, lsev, B, 1, Hq, N, d, 1, s);
+        if (e != hipSuccess)
+            return hip_status(e, "dilated init");
+    }
+    for (int i = 0; i < n_branches; ++i) {
+        const int64_t w = std::min<int64_t>(segment_lengths[i], N), r = dilations[i];
+        const int64_t nfull = N / w, tail = N % w;
+        for (int part = 0; part < 2; ++part) {
+            const int64_t nseg = part == 0 ? nfull : (tail > 0 ? 1 : 0);
+            const int64_t seglen = part == 0 ? w : tail;
+            if (nseg == 0)
+                continue;
+            const int64_t base = part == 0 ? 0 : nfull * w;   // first row of the part
+            const int64_t rows = (seglen + r - 1) / r;        // selected rows per segment
+            auto sub = [&](View vv, int64_t es, int64_t sn) {
+                View x = vv;
+                x.ptr = (const char *)vv.ptr + base * sn * es;
+                x.ss = w * sn;
+                x.sn = r * sn;
+                return x;
+            };
+            FwdParams p;
+            p.q = sub(view_of(q), 2, q->stride_n);
+            p.k = sub(view_of(k), 2, k->stride_n);
+            p.v = sub(view_of(v), 2, v->stride_n);
+            p.o = sub(acc, 4, acc.sn);
+            p.lse = sub(lsev, 4, lse->stride_n);
+            p.B = B;
+            p.S = (int)nseg;
+            p.Hq = Hq;
+            p.Hkv = (int)k->h;
+            p.Nq = p.Nk = (int)rows;
+            clamp_delta(causal ? 0 : SEQATTN_NONCAUSAL, rows, rows, &p.delta, &p.noncausal);
+            p.scale = scale;
+            p.accumulate = (i == 0 && first_writes) ? 0 : 1;
+            p.o_f32 = 1;
+            hipError_t e = launch_fwd_bf16(p, d, s);
+            if (e != hipSuccess)
+                return hip_status(e, "dilated branch launch");
+        }
+    }
+    if (o_bf16) {
+        hipError_t e = launch_cast_bf16(acc, view_of(o), B, Hq, N, d, s);
+        if (e != hipSuccess)
+            return hip_status(e, "dilated cast");
+    }
+    return ok();
+}
+
+int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, const seqattn_tensor *o,
+                             const seqattn_tensor *lse, const seqattn_tensor *d_o,
+                             int64_t causal_offset, float softmax_scale, uint32_t flags,
+                             seqattn_tensor *dq, seqattn_tensor *dk, seqattn_tensor *dv,
+                             void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    int st;
+    if ((st = check_qkv(q, k, v, false)))
+        return st;
+    if ((st = check_tensor(o, "o", false)) || (st = check_tensor(lse, "lse", true)) ||
+        (st = check_tensor(d_o, "d_o", false)) || (st = check_tensor(dq, "dq", false)) ||
+        (st = check_tensor(dk, "dk", false)) || (st = check_tensor(dv, "dv", false)))
+        return st;
+    if (q->dtype != SEQATTN_BF16)
+        return fail(SEQATTN_ERR_UNSUPPORTED, "backward takes bf16 q/k/v");
+    if (d_o->dtype != SEQATTN_BF16)
+        return fail(SEQATTN_ERR_DTYPE, "d_o must be bf16");
+    if (dq->dtype != SEQATTN_F32)
+        return fail(SEQATTN_ERR_DTYPE, "dq must be fp32 (accumulated)");
+    if (flags != 0)
+        return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const seqattn_tensor *qlike[3] = {o, d_o, dq};
+    for (const seqattn_tensor *t : qlike)
+        if (t->b != q->b || t->h != q->h || t->n != q->n || t->d != q->d)
+            return fail(SEQATTN_ERR_SHAPE, "o, d_o, dq must be [B, Hq, Nq, d]");
+    if (lse->b != q->b || lse->h != q->h || lse->n != q->n)
+        return fail(SEQATTN_ERR_SHAPE, "lse must be [B, Hq, Nq, 1]");
+    const seqattn_tensor *klike[2] = {dk, dv};
+    for (const seqattn_tensor *t : klike)
+        if (t->b != k->b || t->h != k->h || t->n != k->n || t->d != k->d)
+            return fail(SEQATTN_ERR_SHAPE, "dk, dv must be [B, Hkv, Nk, d]");
+    const seqattn_tensor *ins[6] = {q, k, v, o, lse, d_o};
+    const seqattn_tensor *outs[3] = {dq, dk, dv};
+    for (const seqattn_tensor *a : outs) {
+        for (const seqattn_tensor *b : ins)
+            if (overlaps(a, b))
+                return fail(SEQATTN_ERR_ALIAS, "a gradient overlaps an input");
+        for (const seqattn_tensor *b : outs)
+            if (a != b && overlaps(a, b))
+                return fail(SEQATTN_ERR_ALIAS, "gradients overlap each other");
+    }
+    const size_t need = seqattn_workspace_size(SEQATTN_OP_SEGMENT_BWD, q, k, 0);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(SEQATTN_ERR_WORKSPACE, "need %zu bytes of workspace", need);
+    if (workspace && (uintptr_t)workspace % 16)
+        return fail(SEQATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+
+    BwdParams p;
+    p.q = view_of(q);
+    p.k = view_of(k);
+    p.v = view_of(v);
+    p.o = view_of(o);
+    p.lse = view_of(lse);
+    p.dout = view_of(d_o);
+    p.dq = view_of(dq);
+    p.dk = view_of(dk);
+    p.dv = view_of(dv);
+    p.dvec = (float *)workspace;
+    p.B = (int)q->b;
+    p.Hq = (int)q->h;
+    p.Hkv = (int)k->h;
+    p.Nq = (int)q->n;
+    p.Nk = (int)k->n;
+    p.d = (int)q->d;
+    clamp_delta(causal_offset, q->n, k->n, &p.delta, &p.noncausal);
+    p.scale = pick_scale(softmax_scale, q->d);
+    p.o_f32 = o->dtype == SEQATTN_F32;
+    p.dk_f32 = dk->dtype == SEQATTN_F32;
+    p.dv_f32 = dv->dtype == SEQATTN_F32;
+    if (p.B == 0 || p.Hkv == 0 || (p.Nk == 0 && p.Nq == 0))
+        return ok();
+    return hip_status(launch_bwd_bf16(p, stream_of(hip_stream)), "attn_segment_bwd launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,394 @@
+// Segment backward, bf16 inputs, MFMA path for gfx950.
+//
+// Gradients of one (query block, KV segment) pair given the GLOBAL softmax
+// statistics (LSE and O merged over every segment the queries saw): a device
+// that attended to a segment forms the gradients for that segment's keys and
+// values ("LongNet: Scaling Transformers to 1,000,000,000 Tokens",
+// Distributed Trainer: the backward turns the all-gather into a
+// reduce-scatter).  With P = exp(sigma*S - LSE) and D_i = dO_i . O_i:
+//   dV = P^T dO,  dS = P o (dO V^T - D),  dK = sigma dS^T Q,  dQ += sigma dS K.
+//
+// Work decomposition
+//   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row);
+//   * bwd_main: one workgroup = 4 waves = 128 keys of one (batch, KV head);
+//     each wave keeps its 32 keys' K and V rows in VGPRs and its dK^T, dV^T
+//     accumulators (fp32) for the whole kernel, and loops over the query
+//     heads sharing the KV head and over the visible 64-row query tiles.
+//     Per tile the scores are recomputed as S = Q K^T with keys in lane
+//     columns (v_mfma_f32_32x32x16_bf16), so P and dS are directly the B
+//     operands of dV^T += dO^T P and dK^T += Q^T dS; Q^T and dO^T are staged
+//     transposed in LDS in the matching row interleave.  dS goes through LDS
+//     once more for dQ = dS K (K^T staged in LDS once per workgroup), which
+//     is added to the fp32 dQ with hardware float atomics.
+#include "common.h"
+
+namespace seqattn {
+namespace {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBKV = 32 * kWaves;  // keys per workgroup
+constexpr int kBQ = 64;            // query rows per iteration
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline unsigned pack_bf16(float a, float b)
+{
+    bf16 x = (bf16)a, y = (bf16)b;
+    return (unsigned)__builtin_bit_cast(unsigned short, x) |
+           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+// Same 16-row interleave as the forward's V^T: within 16 rows the order is
+// [0-3, 8-11, 4-7, 12-15] (matches the accumulator rows each lane half holds).
+__device__ inline int perm_pos(int g4)
+{
+    const int q4 = g4 & 3;
+    return (g4 >> 2) * 16 + (((q4 & 1) << 1) | (q4 >> 1)) * 4;
+}
+
+__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// D_i = sum_c dO_ic O_ic; 16 lanes per row, d/16 elements per lane.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
+{
+    const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
+    const int sub = threadIdx.x & 15;
+    const int per = p.d / 16;  // 4 or 8
+    float acc = 0.f;
+    if (row < rows) {
+        const int i = (int)(row % p.Nq);
+        const int64_t bh = row / p.Nq;
+        const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh +
+                         (int64_t)i * p.dout.sn + sub * per;
+        const int64_t ooff = b * p.o.sb + h * p.o.sh + (int64_t)i * p.o.sn + sub * per;
+        for (int c = 0; c < per; c += 4) {
+            const uint2 g = *(const uint2 *)(dO + c);
+            float o0, o1, o2, o3;
+            if (p.o_f32) {
+                const float4 x = *(const float4 *)((const float *)p.o.ptr + ooff + c);
+                o0 = x.x; o1 = x.y; o2 = x.z; o3 = x.w;
+            } else {
+                const uint2 x = *(const uint2 *)((const bf16 *)p.o.ptr + ooff + c);
+                o0 = bf16_lo(x.x); o1 = bf16_hi(x.x); o2 = bf16_lo(x.y); o3 = bf16_hi(x.y);
+            }
+            acc += bf16_lo(g.x) * o0 + bf16_hi(g.x) * o1 + bf16_lo(g.y) * o2 + bf16_hi(g.y) * o3;
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+        acc += __shfl_xor(acc, m, 16);
+    if (row < rows && sub == 0)
+        p.dvec[row] = acc;
+}
+
+template <int D>
+struct BCfg {
+    static constexpr int QSTR = D + 8;        // Q / dO row pitch (bf16)
+    static constexpr int TSTR = kBQ + 8;      // Q^T / dO^T row pitch
+    static constexpr int SSTR = kBKV + 8;     // dS row pitch
+    static constexpr int KTSTR = kBKV + 8;    // K^T row pitch
+    static constexpr int QBLK = (kBQ / 4) * (D / 8);  // 4x8 blocks per Q tile
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
+{
+    using C = BCfg<D>;
+    __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * C::QSTR];
+    __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * C::QSTR];
+    __shared__ __attribute__((aligned(16))) bf16 QTs[D * C::TSTR];
+    __shared__ __attribute__((aligned(16))) bf16 dOTs[D * C::TSTR];
+    __shared__ __attribute__((aligned(16))) bf16 dSs[kBQ * C::SSTR];
+    __shared__ __attribute__((aligned(16))) bf16 KTs[D * C::KTSTR];
+    __shared__ float lse2s[kBQ];
+    __shared__ float Dsh[kBQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+
+    const int nkt = (p.Nk + kBKV - 1) / kBKV;
+    const int kt = (int)(blockIdx.x % nkt);
+    const int bg = (int)(blockIdx.x / nkt);
+    const int g = bg % p.Hkv, b = bg / p.Hkv;
+    const int k0 = kt * kBKV;
+    const int kw0 = k0 + wave * 32;
+    const int key = kw0 + l32;  // this lane's key (accumulator column)
+
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + g * p.k.sh;
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + g * p.v.sh;
+
+    // K^T tile of the workgroup in LDS (natural key order), for dQ = dS K
+    for (int blk = tid; blk < (kBKV / 4) * (D / 8); blk += kThreads) {
+        const int kg = blk % (kBKV / 4), dc = blk / (kBKV / 4);
+        unsigned a[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = k0 + kg * 4 + u;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (j < p.Nk)
+                x = *(const u32x4 *)(K + (int64_t)j * p.k.sn + dc * 8);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                a[u][m] = x[m];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint2 lo, hi;
+            lo.x = (a[0][m] & 0xffffu) | (a[1][m] << 16);
+            lo.y = (a[2][m] & 0xffffu) | (a[3][m] << 16);
+            hi.x = (a[0][m] >> 16) | (a[1][m] & 0xffff0000u);
+            hi.y = (a[2][m] >> 16) | (a[3][m] & 0xffff0000u);
+            *(uint2 *)(&KTs[(dc * 8 + 2 * m) * C::KTSTR + kg * 4]) = lo;
+            *(uint2 *)(&KTs[(dc * 8 + 2 * m + 1) * C::KTSTR + kg * 4]) = hi;
+        }
+    }
+
+    // this wave's K and V rows as B operands (k = d): lane holds key `key`,
+    // d = 16kk + 8hl .. +8
+    bf16x8 kB[D / 16], vB[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        if (key < p.Nk) {
+            xk = *(const u32x4 *)(K + (int64_t)key * p.k.sn + kk * 16 + hl * 8);
+            xv = *(const u32x4 *)(V + (int64_t)key * p.v.sn + kk * 16 + hl * 8);
+        }
+        kB[kk] = __builtin_bit_cast(bf16x8, xk);
+        vB[kk] = __builtin_bit_cast(bf16x8, xv);
+    }
+
+    f32x16 dKacc[D / 32], dVacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            dKacc[i][e] = dVacc[i][e] = 0.f;
+
+    const float c = p.scale * kLog2e;
+    const int group = p.Hq / p.Hkv;
+    const int nqt = (p.Nq + kBQ - 1) / kBQ;
+    int qt_begin = 0;
+    if (!p.noncausal) {
+        const int first_q = max(0, k0 - p.delta);  // smallest query seeing key k0
+        qt_begin = min(nqt, first_q / kBQ);
+    }
+
+    for (int hh = 0; hh < group; ++hh) {
+        const int h = g * group + hh;
+        const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + h * p.q.sh;
+        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh;
+        const float *LSE = (const float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh;
+        const float *Dv = p.dvec + ((int64_t)b * p.Hq + h) * p.Nq;
+        float *dQ = (float *)p.dq.ptr + b * p.dq.sb + h * p.dq.sh;
+
+        for (int qt = qt_begin; qt < nqt; ++qt) {
+            const int q0 = qt * kBQ;
+            __syncthreads();
+            // ---- stage Q, dO tiles (row-major and transposed/interleaved) ----
+            for (int job = tid; job < 2 * C::QBLK; job += kThreads) {
+                const bool isq = job < C::QBLK;
+                const int blk = isq ? job : job - C::QBLK;
+                const int qg = blk % (kBQ / 4), dc = blk / (kBQ / 4);
+                const bf16 *src = isq ? Q : dO;
+                const int64_t sn = isq ? p.q.sn : p.dout.sn;
+                bf16 *rm = isq ? Qs : dOs;
+                bf16 *tr = isq ? QTs : dOTs;
+                unsigned a[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = q0 + qg * 4 + u;
+                    u32x4 x = {0u, 0u, 0u, 0u};
+                    if (i < p.Nq)
+                        x = *(const u32x4 *)(src + (int64_t)i * sn + dc * 8);
+                    *(u32x4 *)(&rm[(qg * 4 + u) * C::QSTR + dc * 8]) = x;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        a[u][m] = x[m];
+                }
+                const int pos = perm_pos(qg);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    uint2 lo, hi;
+                    lo.x = (a[0][m] & 0xffffu) | (a[1][m] << 16);
+                    lo.y = (a[2][m] & 0xffffu) | (a[3][m] << 16);
+                    hi.x = (a[0][m] >> 16) | (a[1][m] & 0xffff0000u);
+                    hi.y = (a[2][m] >> 16) | (a[3][m] & 0xffff0000u);
+                    *(uint2 *)(&tr[(dc * 8 + 2 * m) * C::TSTR + pos]) = lo;
+                    *(uint2 *)(&tr[(dc * 8 + 2 * m + 1) * C::TSTR + pos]) = hi;
+                }
+            }
+            if (tid < kBQ) {
+                const int i = q0 + tid;
+                float l2 = INFINITY, dd = 0.f;  // +inf: row contributes P = 0
+                if (i < p.Nq) {
+                    const float lv = LSE[(int64_t)i * p.lse.sn];
+                    if (lv != -INFINITY)
+                        l2 = lv * kLog2e;
+                    dd = Dv[i];
+                }
+                lse2s[tid] = l2;
+                Dsh[tid] = dd;
+            }
+            __syncthreads();
+
+            // ---- S = Q K^T, dP = dO V^T for 2 blocks of 32 queries ----
+            const bool need_mask = (k0 + kBKV > p.Nk) || (q0 + kBQ > p.Nq) ||
+                                   (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
+            unsigned pP[2][8], pS[2][8];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x16 s, dp;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    s[e] = dp[e] = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const bf16x8 aq = *(const bf16x8 *)(&Qs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                    const bf16x8 ad = *(const bf16x8 *)(&dOs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
+                }
+                // element e: query row qb*32 + 8(e/4) + 4hl + e%4 of the tile
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int r0 = qb * 32 + gq * 8 + hl * 4;
+                    const float4 l2 = *(const float4 *)(&lse2s[r0]);
+                    const float4 dd = *(const float4 *)(&Dsh[r0]);
+                    const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+                    const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
+                    float pv[4], sv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = gq * 4 + u;
+                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
+                        if (need_mask) {
+                            const int qi = q0 + r0 + u;
+                            const bool vis = key < p.Nk && qi < p.Nq &&
+                                             (p.noncausal || key - qi <= p.delta);
+                            pe = vis ? pe : 0.f;
+                        }
+                        pv[u] = pe;
+                        sv[u] = pe * (dp[e] - dv[u]);
+                    }
+                    pP[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
+                    pP[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
+                    pS[qb][gq * 2 + 0] = pack_bf16(sv[0], sv[1]);
+                    pS[qb][gq * 2 + 1] = pack_bf16(sv[2], sv[3]);
+                    // dS to LDS, [query][key] (natural order) for dQ
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const bf16 x = (bf16)sv[u];
+                        dSs[(r0 + u) * C::SSTR + wave * 32 + l32] = x;
+                    }
+                }
+            }
+
+            // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 64 query rows) ----
+#pragma unroll
+            for (int ks = 0; ks < kBQ / 16; ++ks) {
+                const int qb = ks >> 1, half = ks & 1;
+                u32x4 wp = {pP[qb][half * 4 + 0], pP[qb][half * 4 + 1], pP[qb][half * 4 + 2],
+                            pP[qb][half * 4 + 3]};
+                u32x4 ws = {pS[qb][half * 4 + 0], pS[qb][half * 4 + 1], pS[qb][half * 4 + 2],
+                            pS[qb][half * 4 + 3]};
+                const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
+                const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) {
+                    const bf16x8 ad = *(const bf16x8 *)(&dOTs[(i * 32 + l32) * C::TSTR + ks * 16 + hl * 8]);
+                    const bf16x8 aq = *(const bf16x8 *)(&QTs[(i * 32 + l32) * C::TSTR + ks * 16 + hl * 8]);
+                    dVacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bp, dVacc[i], 0, 0, 0);
+                    dKacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bs, dKacc[i], 0, 0, 0);
+                }
+            }
+            __syncthreads();
+
+            // ---- dQ[q][d] += sigma * sum_key dS[q][key] K[key][d] ----
+            constexpr int nblk = (kBQ / 32) * (D / 32);
+            for (int ob = wave; ob < nblk; ob += kWaves) {
+                const int qb = ob % (kBQ / 32), db = ob / (kBQ / 32);
+                f32x16 acc;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[e] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < kBKV / 16; ++ks) {
+                    const bf16x8 a = *(const bf16x8 *)(&dSs[(qb * 32 + l32) * C::SSTR + ks * 16 + hl * 8]);
+                    const bf16x8 bk = *(const bf16x8 *)(&KTs[(db * 32 + l32) * C::KTSTR + ks * 16 + hl * 8]);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, acc, 0, 0, 0);
+                }
+                const int dcol = db * 32 + l32;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int qi = q0 + qb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                    if (qi < p.Nq)
+                        unsafeAtomicAdd(dQ + (int64_t)qi * p.dq.sn + dcol, acc[e] * p.scale);
+                }
+            }
+        }
+    }
+
+    // ---- write dK = sigma dK^T^T, dV (key rows, 4 consecutive d per store) ----
+    if (key >= p.Nk)
+        return;
+    const int64_t krow_k = b * p.dk.sb + g * p.dk.sh + (int64_t)key * p.dk.sn;
+    const int64_t krow_v = b * p.dv.sb + g * p.dv.sh + (int64_t)key * p.dv.sn;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = i * 32 + gq * 8 + hl * 4;
+            const float k0v = dKacc[i][gq * 4 + 0] * p.scale, k1v = dKacc[i][gq * 4 + 1] * p.scale;
+            const float k2v = dKacc[i][gq * 4 + 2] * p.scale, k3v = dKacc[i][gq * 4 + 3] * p.scale;
+            const float v0 = dVacc[i][gq * 4 + 0], v1 = dVacc[i][gq * 4 + 1];
+            const float v2 = dVacc[i][gq * 4 + 2], v3 = dVacc[i][gq * 4 + 3];
+            if (p.dk_f32) {
+                float4 w = {k0v, k1v, k2v, k3v};
+                *(float4 *)((float *)p.dk.ptr + krow_k + d0) = w;
+            } else {
+                uint2 w = {pack_bf16(k0v, k1v), pack_bf16(k2v, k3v)};
+                *(uint2 *)((bf16 *)p.dk.ptr + krow_k + d0) = w;
+            }
+            if (p.dv_f32) {
+                float4 w = {v0, v1, v2, v3};
+                *(float4 *)((float *)p.dv.ptr + krow_v + d0) = w;
+            } else {
+                uint2 w = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
+                *(uint2 *)((bf16 *)p.dv.ptr + krow_v + d0) = w;
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st)
+{
+    const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+    if (rows > 0) {
+        const int64_t blocks = (rows * 16 + 255) / 256;
+        hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int nkt = (p.Nk + kBKV - 1) / kBKV;
+    const int64_t grid = (int64_t)nkt * p.B * p.Hkv;
+    if (grid == 0)
+        return hipSuccess;
+    if (p.d == 128)
+        hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL(bwd_main_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace seqattn

@@ -1,0 +1,57 @@
+// Internal parameter blocks shared by the ABI layer and the HIP kernels.
+// Not part of the public C ABI (include/seqattn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace seqattn {
+
+// One strided view [batch][seg][head][row][d] of a tensor (element strides;
+// d contiguous).  `seg` is an extra batch-like dimension used by the dilated
+// path (segments of one branch); it is 1 for a plain segment call.
+struct View {
+    const void *ptr;
+    int64_t sb, ss, sh, sn;
+};
+
+// Forward over (query block, KV segment) pairs.
+struct FwdParams {
+    View q, k, v, o, lse;
+    int B, S, Hq, Hkv;   // batch, segments per batch entry, heads
+    int Nq, Nk;          // rows per (b, s, h)
+    int delta;           // visibility: key j <= query i + delta (clamped)
+    int noncausal;       // 1: every key visible
+    float scale;         // softmax scale (natural units)
+    int accumulate;      // fused LSE-merge epilogue into fp32 (o, lse)
+    int o_f32;           // output element type: 1 fp32, 0 bf16
+};
+
+struct MergeParams {
+    View oa, la, ob, lb;
+    int B, H, N, d;
+    int ob_f32;
+};
+
+struct BwdParams {
+    View q, k, v, o, lse, dout, dq, dk, dv;
+    float *dvec;           // workspace: D_i = sum_c dO_ic O_ic, [B*Hq*Nq]
+    int B, Hq, Hkv, Nq, Nk, d;
+    int delta, noncausal;
+    float scale;
+    int o_f32, dk_f32, dv_f32;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t st);
+hipError_t launch_lse_merge(const MergeParams &p, hipStream_t st);
+// Writes the empty partial (O = 0, LSE = -inf) into an fp32/bf16 o view and lse.
+hipError_t launch_fill_empty(const View &o, const View &lse, int B, int S, int H,
+                             int N, int d, int o_f32, hipStream_t st);
+// Casts an fp32 [B][H][N][d] view to a bf16 view.
+hipError_t launch_cast_bf16(const View &src, const View &dst, int B, int H, int N,
+                            int d, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st);
+
+}  // namespace seqattn

@@ -1,0 +1,121 @@
+"""Single-GPU emulation of the sequence-parallel schedules (host loops only).
+
+Every step is one library call; these functions only choose which (query
+block, KV segment) pairs are issued, in which order, with which offset.
+
+* Ring attention ("Boosting Spec Eagle: USP For Long-Context Training", The
+  Solution: devices in a ring, each with a slice, passing blocks to their
+  neighbours): rank r holds query block r; at step t it holds KV block
+  j = (r - t) mod P, attends to it with causal offset (r - j) * block and merges
+  the partial into its running (O, LSE).  Blocks entirely in the causal future
+  are skipped.
+* DeepSpeed-Ulysses ("DeepSpeed-Ulysses" article, Wie DeepSpeed-Ulysses
+  funktioniert: after the all-to-all a GPU sees the whole sequence): one call
+  on the GPU's head subset at full length.
+* USP ("Boosting Spec Eagle ...", The Solution: Ulysses and Ring combined):
+  a head subset swept over KV blocks like a ring rank, forward and backward.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import attn_segment_bwd, attn_segment_fwd
+
+
+def ring_order(rank: int, P: int):
+    """KV block held by `rank` at steps t = 0..P-1 of a ring."""
+    return [(rank - t) % P for t in range(P)]
+
+
+def sweep_fwd(q, k, v, n_blocks: int, q_block: int, causal: bool, out, lse, scale=None):
+    """Forward of one query block against K/V cut into n_blocks equal blocks.
+
+    q is the query block whose first row sits at global position
+    q_block * (Nk / n_blocks); out (fp32) and lse receive the merged result.
+    Returns the number of launches issued.
+    """
+    nk = k.shape[-2]
+    if nk % n_blocks:
+        raise ValueError("K/V length must split into equal blocks")
+    blk = nk // n_blocks
+    q_start = q_block * blk
+    first = True
+    launches = 0
+    for j in ring_order(q_block, n_blocks):
+        k_start = j * blk
+        delta = q_start - k_start
+        if causal and delta + q.shape[-2] - 1 < 0:
+            continue  # every key of block j is in the future of every query
+        kj = k[..., k_start:k_start + blk, :]
+        vj = v[..., k_start:k_start + blk, :]
+        attn_segment_fwd(q, kj, vj, causal_offset=delta if causal else None, scale=scale,
+                         out=out, lse=lse, accumulate=not first)
+        first = False
+        launches += 1
+    if first:  # nothing visible at all
+        out.zero_()
+        lse.fill_(float("-inf"))
+    return launches
+
+
+def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None):
+    """All P ranks of a ring, run one after another on one GPU.
+
+    q, k, v: [B,H,N,d]; rank r owns rows [r*N/P, (r+1)*N/P).  Returns the
+    merged fp32 output [B,H,N,d] and LSE [B,H,N] of the whole sequence.
+    """
+    n = q.shape[-2]
+    blk = n // P
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    for r in range(P):
+        rows = slice(r * blk, (r + 1) * blk)
+        sweep_fwd(q[..., rows, :], k, v, P, r, causal, out[..., rows, :], lse[..., rows],
+                  scale=scale)
+    return out, lse
+
+
+def ulysses_fwd(q, k, v, causal: bool = True, scale=None, out_dtype=None):
+    """Ulysses share: the GPU's head subset, full sequence, one call."""
+    return attn_segment_fwd(q, k, v, causal_offset=0 if causal else None, scale=scale,
+                            out_dtype=out_dtype)
+
+
+def usp_fwd_bwd(q, k, v, d_o, n_blocks: int, q_block: int, causal: bool = True,
+                scale=None, grad_dtype=torch.float32):
+    """USP share: forward sweep over KV blocks, then the backward sweep.
+
+    Returns (o, lse, dq, dk, dv); dk, dv cover all of K/V ([B,Hkv,Nk,d]).
+    """
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    sweep_fwd(q, k, v, n_blocks, q_block, causal, out, lse, scale=scale)
+    dq, dk, dv = usp_bwd(q, k, v, out, lse, d_o, n_blocks, q_block, causal, scale,
+                         grad_dtype=grad_dtype)
+    return out, lse, dq, dk, dv
+
+
+def usp_bwd(q, k, v, out, lse, d_o, n_blocks: int, q_block: int, causal: bool = True,
+            scale=None, grad_dtype=torch.float32, dq=None, dk=None, dv=None):
+    """Backward sweep: dQ accumulates over blocks, each block writes its dK/dV."""
+    nk = k.shape[-2]
+    blk = nk // n_blocks
+    q_start = q_block * blk
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=k.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=v.device)
+    for j in ring_order(q_block, n_blocks):
+        k_start = j * blk
+        rows = slice(k_start, k_start + blk)
+        delta = q_start - k_start
+        if causal and delta + q.shape[-2] - 1 < 0:
+            dk[..., rows, :].zero_()
+            dv[..., rows, :].zero_()
+            continue
+        attn_segment_bwd(q, k[..., rows, :], v[..., rows, :], out, lse, d_o,
+                         causal_offset=delta if causal else None, scale=scale, dq=dq,
+                         dk=dk[..., rows, :], dv=dv[..., rows, :])
+    return dq, dk, dv

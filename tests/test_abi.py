@@ -1,0 +1,181 @@
+"""The C ABI on the CPU: the library loads, exports what include/seqattn.h
+declares, and every validation error is returned before any HIP call (fake,
+never dereferenced device addresses are used)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_sequence_exact_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seqattn.h")
+
+OK, ENULL, EDTYPE, ESHAPE, ESTRIDE, EALIAS, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from long_sequence_exact_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(seqattn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_ops_and_helpers():
+    names = declared_functions()
+    for f in ("seqattn_attn_segment_fwd", "seqattn_lse_merge", "seqattn_dilated_attn_fwd",
+              "seqattn_attn_segment_bwd"):
+        assert f in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (seqattn_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert L.seqattn_version() == 100
+
+
+BASE = 0x7f0000000000  # fake, 256-byte aligned device addresses (never touched)
+
+
+def T(addr, dtype, b, h, n, d, contiguous=True, **kw):
+    t = _lib.Tensor(addr, dtype, b, h, n, d, h * n * d, n * d, d)
+    for key, val in kw.items():
+        setattr(t, key, val)
+    return t
+
+
+def LSE(addr, b, h, n):
+    return _lib.Tensor(addr, _lib.F32, b, h, n, 1, h * n, n, 1)
+
+
+def qkvo(dtype=_lib.BF16, hq=4, hkv=2, nq=256, nk=512, d=128, odtype=None):
+    step = 1 << 30
+    q = T(BASE, dtype, 1, hq, nq, d)
+    k = T(BASE + step, dtype, 1, hkv, nk, d)
+    v = T(BASE + 2 * step, dtype, 1, hkv, nk, d)
+    o = T(BASE + 3 * step, odtype or dtype, 1, hq, nq, d)
+    lse = LSE(BASE + 4 * step, 1, hq, nq)
+    return q, k, v, o, lse
+
+
+def fwd(L, q, k, v, o, lse, delta=0, flags=0):
+    r = ctypes.byref
+    return L.seqattn_attn_segment_fwd(r(q) if q is not None else None, r(k), r(v), delta, 0.0,
+                                      flags, r(o), r(lse), None)
+
+
+def test_fwd_validation_errors(L):
+    q, k, v, o, lse = qkvo()
+    assert fwd(L, None, k, v, o, lse) == ENULL
+    q2 = T(BASE, _lib.F32, 1, 4, 256, 128)
+    assert fwd(L, q2, k, v, o, lse) == EDTYPE
+    qbad = T(BASE, 7, 1, 4, 256, 128)
+    assert fwd(L, qbad, k, v, o, lse) == EDTYPE
+    q96, k96, v96, o96, l96 = qkvo(d=96)
+    assert fwd(L, q96, k96, v96, o96, l96) == ESHAPE
+    q3, k3, v3, o3, l3 = qkvo(hq=6, hkv=4)
+    assert fwd(L, q3, k3, v3, o3, l3) == ESHAPE
+    qm = T(BASE + 8, _lib.BF16, 1, 4, 256, 128)
+    assert fwd(L, qm, k, v, o, lse) == ESTRIDE
+    qs = T(BASE, _lib.BF16, 1, 4, 256, 128, stride_n=132)
+    assert fwd(L, qs, k, v, o, lse) == ESTRIDE
+    neg = T(BASE, _lib.BF16, 1, 4, -1, 128)
+    assert fwd(L, neg, k, v, o, lse) == ESHAPE
+    oal = T(BASE + 64, _lib.BF16, 1, 4, 256, 128)  # overlaps q
+    assert fwd(L, q, k, v, oal, lse) == EALIAS
+    assert fwd(L, q, k, v, o, lse, flags=1) == EDTYPE  # accumulate needs fp32 o
+    assert fwd(L, q, k, v, o, lse, flags=8) == EUNSUP
+    lbad = _lib.Tensor(lse.data, _lib.BF16, 1, 4, 256, 1, 1024, 256, 1)
+    assert fwd(L, q, k, v, o, lbad) == EDTYPE
+    lshape = LSE(lse.data, 1, 4, 255)
+    assert fwd(L, q, k, v, o, lshape) == ESHAPE
+    kv_mis = T(BASE + (1 << 30), _lib.BF16, 1, 2, 500, 128)
+    assert fwd(L, q, kv_mis, v, o, lse) == ESHAPE
+    # fp32 inputs need an fp32 output
+    qf, kf, vf, of, lf = qkvo(dtype=_lib.F32, odtype=_lib.BF16)
+    assert fwd(L, qf, kf, vf, of, lf) == EDTYPE
+    msg = L.seqattn_last_error().decode()
+    assert "fp32" in msg
+    assert L.seqattn_status_string(EALIAS).decode() == "output aliases an input"
+
+
+def test_fwd_empty_query_block_returns_ok_without_launch(L):
+    q, k, v, o, lse = qkvo(nq=0)
+    assert fwd(L, q, k, v, o, lse) == OK
+
+
+def test_lse_merge_validation_errors(L):
+    r = ctypes.byref
+    step = 1 << 28
+    oa = T(BASE, _lib.F32, 1, 2, 64, 128)
+    la = LSE(BASE + step, 1, 2, 64)
+    ob = T(BASE + 2 * step, _lib.BF16, 1, 2, 64, 128)
+    lb = LSE(BASE + 3 * step, 1, 2, 64)
+    oa16 = T(BASE, _lib.BF16, 1, 2, 64, 128)
+    assert L.seqattn_lse_merge(r(oa16), r(la), r(ob), r(lb), None) == EDTYPE
+    ob_bad = T(BASE + 2 * step, _lib.BF16, 1, 2, 63, 128)
+    assert L.seqattn_lse_merge(r(oa), r(la), r(ob_bad), r(lb), None) == ESHAPE
+    assert L.seqattn_lse_merge(r(oa), r(la), r(oa), r(lb), None) == EALIAS
+    assert L.seqattn_lse_merge(None, r(la), r(ob), r(lb), None) == ENULL
+
+
+def test_dilated_validation_errors(L):
+    r = ctypes.byref
+    q, k, v, o, lse = qkvo(hq=2, hkv=2, nq=512, nk=512, d=64, odtype=_lib.BF16)
+    w = (ctypes.c_int64 * 2)(128, 512)
+    rr = (ctypes.c_int64 * 2)(1, 2)
+    call = lambda w_, r_, nb, flags=0, ws=None, wsb=0, oo=o: L.seqattn_dilated_attn_fwd(
+        r(q), r(k), r(v), w_, r_, nb, 0.0, flags, r(oo), r(lse), ws, wsb, None)
+    assert call(w, rr, 0) == ESHAPE
+    assert call(None, rr, 2) == ENULL
+    w0 = (ctypes.c_int64 * 2)(0, 512)
+    assert call(w0, rr, 2) == ESHAPE
+    assert call(w, rr, 2, flags=1) == EUNSUP
+    assert call(w, rr, 2) == EWS  # bf16 o needs the fp32 workspace
+    need = L.seqattn_workspace_size(_lib.OP_DILATED_FWD, r(q), r(o), 2)
+    assert need == 2 * 512 * 64 * 4
+    assert call(w, rr, 2, ws=BASE + (5 << 30), wsb=need - 1) == EWS
+    qn = T(BASE, _lib.BF16, 1, 2, 500, 64)
+    assert L.seqattn_dilated_attn_fwd(r(qn), r(k), r(v), w, rr, 2, 0.0, 0, r(o), r(lse),
+                                      None, 0, None) == ESHAPE
+
+
+def test_bwd_validation_errors(L):
+    r = ctypes.byref
+    step = 1 << 30
+    q, k, v, o, lse = qkvo()
+    do = T(BASE + 5 * step, _lib.BF16, 1, 4, 256, 128)
+    dq = T(BASE + 6 * step, _lib.F32, 1, 4, 256, 128)
+    dk = T(BASE + 7 * step, _lib.F32, 1, 2, 512, 128)
+    dv = T(BASE + 8 * step, _lib.F32, 1, 2, 512, 128)
+    need = L.seqattn_workspace_size(_lib.OP_SEGMENT_BWD, r(q), r(k), 0)
+    assert need == 4 * 256 * 4
+    ws = BASE + 9 * step
+
+    def call(q_=q, dq_=dq, dk_=dk, dv_=dv, ws_=ws, wsb=need, flags=0):
+        return L.seqattn_attn_segment_bwd(r(q_), r(k), r(v), r(o), r(lse), r(do), 0, 0.0,
+                                          flags, r(dq_), r(dk_), r(dv_), ws_, wsb, None)
+    assert call(wsb=need - 4) == EWS
+    assert call(ws_=None, wsb=0) == EWS
+    dq16 = T(dq.data, _lib.BF16, 1, 4, 256, 128)
+    assert call(dq_=dq16) == EDTYPE
+    dv_al = T(dk.data + 256, _lib.F32, 1, 2, 512, 128)
+    assert call(dv_=dv_al) == EALIAS
+    dk_bad = T(dk.data, _lib.F32, 1, 2, 511, 128)
+    assert call(dk_=dk_bad) == ESHAPE
+    assert call(flags=1) == EUNSUP
+    qf, kf, vf, _, _ = qkvo(dtype=_lib.F32)
+    assert L.seqattn_attn_segment_bwd(r(qf), r(kf), r(vf), r(o), r(lse), r(do), 0, 0.0, 0,
+                                      r(dq), r(dk), r(dv), ws, need, None) == EUNSUP

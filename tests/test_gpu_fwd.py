@@ -1,0 +1,236 @@
+"""GPU parity of the segment forward, the LSE merge and the sweep drivers.
+
+Every case draws seeded host tensors, runs the HIP path through the C ABI
+(Python binding) and compares with the fp64 oracle on the same values.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_sequence_exact_amd as sa
+from long_sequence_exact_amd import emulate
+from long_sequence_exact_amd.synth import WORKLOADS, draw, sample_rows, workload_inputs
+from tests.parity import LSE_TOL, TOL, assert_parity, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _np32(t):
+    return t.float().numpy()
+
+
+def _delta_arg(delta):
+    return oracle.NONCAUSAL if delta is None else delta
+
+
+# ---------------------------------------------------------------- tiny fp32
+
+def test_tiny_fp32_segments_then_merge():
+    """1 head, d=64, 1024 tokens as 4 KV segments of 256, non-causal, seed 0:
+    per-segment (O, LSE), then lse_merge, equals full attention."""
+    w = WORKLOADS["tiny_fp32_segments"]
+    q, k, v = workload_inputs(w)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    seg = w.nk // w.segments
+    parts = [sa.attn_segment_fwd(qd, kd[..., s * seg:(s + 1) * seg, :],
+                                 vd[..., s * seg:(s + 1) * seg, :])
+             for s in range(w.segments)]
+    acc_o, acc_l = parts[0][0].clone(), parts[0][1].clone()
+    for o_s, l_s in parts[1:]:
+        sa.lse_merge(acc_o, acc_l, o_s, l_s)
+    torch.cuda.synchronize()
+    assert_parity(to_np(acc_o), to_np(acc_l), o_ref, l_ref, torch.float32, what="merge")
+    # the same sweep with the fused merge epilogue
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    for s in range(w.segments):
+        sa.attn_segment_fwd(qd, kd[..., s * seg:(s + 1) * seg, :],
+                            vd[..., s * seg:(s + 1) * seg, :], out=out, lse=lse,
+                            accumulate=s > 0)
+    torch.cuda.synchronize()
+    assert_parity(to_np(out), to_np(lse), o_ref, l_ref, torch.float32, what="fused")
+
+
+# ---------------------------------------------------------- small shapes
+
+CASES = [
+    # (dtype, Hq, Hkv, Nq, Nk, d, delta)
+    (torch.bfloat16, 2, 2, 200, 333, 128, None),
+    (torch.bfloat16, 2, 2, 300, 300, 128, 0),
+    (torch.bfloat16, 4, 1, 257, 513, 128, 100),
+    (torch.bfloat16, 8, 2, 130, 700, 128, 400),
+    (torch.bfloat16, 2, 2, 256, 256, 128, -50),
+    (torch.bfloat16, 3, 3, 129, 64, 128, -200),     # every row masked
+    (torch.bfloat16, 2, 1, 1, 1, 128, 0),
+    (torch.bfloat16, 2, 2, 333, 271, 64, None),
+    (torch.bfloat16, 4, 2, 385, 385, 64, 0),
+    (torch.bfloat16, 2, 2, 100, 1000, 64, 700),
+    (torch.float32, 2, 1, 150, 333, 64, 20),
+    (torch.float32, 2, 2, 65, 97, 128, None),
+    (torch.float32, 1, 1, 70, 70, 128, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,nq,nk,d,delta", CASES)
+def test_segment_fwd_small(dtype, hq, hkv, nq, nk, d, delta):
+    q, k, v = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d)], 1000 + nq + nk, dtype)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=_delta_arg(delta))
+    o, lse = sa.attn_segment_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal_offset=delta,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_parity(to_np(o), to_np(lse), o_ref, l_ref, dtype, what="fp32 out")
+    if dtype == torch.bfloat16:
+        ob, lb = sa.attn_segment_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal_offset=delta)
+        torch.cuda.synchronize()
+        assert ob.dtype == torch.bfloat16
+        assert_parity(to_np(ob), to_np(lb), o_ref, l_ref, dtype, what="bf16 out")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 64)])
+def test_fused_accumulate_two_segments(dtype, d):
+    nq, nk = 300, 520
+    q, k, v = draw([(2, 4, nq, d), (2, 2, nk, d), (2, 2, nk, d)], 77, dtype)
+    delta = 250  # causal: q_start - k_start for the whole key range
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=delta)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    cut = 190  # segments [0, 190) and [190, 520): second one seen from delta-190
+    sa.attn_segment_fwd(qd, kd[..., cut:, :], vd[..., cut:, :], causal_offset=delta - cut,
+                        out=out, lse=lse)
+    sa.attn_segment_fwd(qd, kd[..., :cut, :], vd[..., :cut, :], causal_offset=delta,
+                        out=out, lse=lse, accumulate=True)
+    torch.cuda.synchronize()
+    assert_parity(to_np(out), to_np(lse), o_ref, l_ref, dtype, what="accumulate")
+
+
+def test_empty_inputs():
+    q, k, v = draw([(1, 2, 64, 128), (1, 2, 64, 128), (1, 2, 64, 128)], 5)
+    qd = q.to(DEV)
+    kz = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    o, lse = sa.attn_segment_fwd(qd, kz, kz, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    # accumulating an empty segment leaves the accumulator as it was
+    o2, l2 = sa.attn_segment_fwd(qd, k.to(DEV), v.to(DEV))
+    o3 = o2.float().clone()
+    l3 = l2.clone()
+    sa.attn_segment_fwd(qd, kz, kz, out=o3, lse=l3, accumulate=True)
+    sa.attn_segment_fwd(qd, k.to(DEV), v.to(DEV), causal_offset=-10**12, out=o3, lse=l3,
+                        accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o2.float()) and torch.equal(l3, l2)
+    # empty query block: nothing to do
+    qz = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    o4, l4 = sa.attn_segment_fwd(qz, k.to(DEV), v.to(DEV))
+    assert o4.shape == (1, 2, 0, 128)
+
+
+def test_forward_is_deterministic():
+    q, k, v = [t.to(DEV) for t in draw([(1, 4, 1000, 128)] * 3, 9)]
+    a, la = sa.attn_segment_fwd(q, k, v, causal_offset=0)
+    b, lb = sa.attn_segment_fwd(q, k, v, causal_offset=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ------------------------------------------------------------- lse_merge
+
+@pytest.mark.parametrize("b_dtype", [torch.float32, torch.bfloat16])
+def test_lse_merge_matches_oracle(b_dtype):
+    B, H, N, d = 2, 3, 517, 128
+    oa, ob = draw([(B, H, N, d), (B, H, N, d)], 31, torch.float32)
+    la, lb = draw([(B, H, N), (B, H, N)], 32, torch.float32)
+    la = la * 5
+    lb = lb * 5
+    la[0, 0, :7] = -math.inf     # a empty
+    lb[0, 1, :7] = -math.inf     # b empty
+    la[1, 2, :5] = -math.inf     # both empty
+    lb[1, 2, :5] = -math.inf
+    oa[1, 2, :5] = 0
+    ob[1, 2, :5] = 0
+    ob = ob.to(b_dtype)
+    ro, rl = oracle.lse_merge(oa.numpy(), la.numpy(), ob.float().numpy(), lb.numpy())
+    oad, lad = oa.to(DEV), la.to(DEV)
+    sa.lse_merge(oad, lad, ob.to(DEV), lb.to(DEV))
+    torch.cuda.synchronize()
+    assert_parity(to_np(oad), to_np(lad), ro, rl, torch.float32, what="lse_merge")
+    assert not torch.isnan(oad).any()
+
+
+# ------------------------------------------------------------- sweeps
+
+def test_ring_sweep_matches_full_causal_attention_small():
+    P, blk, H, d = 4, 96, 2, 128
+    n = P * blk
+    q, k, v = draw([(1, H, n, d)] * 3, 41)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=0)
+    o, lse = emulate.ring_fwd(q.to(DEV), k.to(DEV), v.to(DEV), P, causal=True)
+    torch.cuda.synchronize()
+    assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="ring small")
+
+
+def _sampled_check(q, k, v, o, lse, delta, rows_per_head, seed, must_rows=(0, -1)):
+    """Oracle on a seeded row subset of every head; compare the GPU rows."""
+    B, H, N, d = q.shape
+    rows = []
+    for h in range(H):
+        for i in sample_rows(N, rows_per_head, seed + h, must=must_rows):
+            rows.append(h * N + i)
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=delta, rows=rows)
+    o_g = to_np(o).reshape(-1, d)[rows]
+    l_g = to_np(lse).reshape(-1)[rows]
+    return o_g, l_g, o_ref, l_ref, rows // N
+
+
+def test_ring_16k_full_size_sampled():
+    """32 heads, d=128, 16384 tokens, causal, 8 ranks x 2048 rows swept over 8
+    KV segments with fused merges; sampled rows against the oracle."""
+    w = WORKLOADS["ring_16k_bf16"]
+    q, k, v = workload_inputs(w)
+    o, lse = emulate.ring_fwd(q.to(DEV), k.to(DEV), v.to(DEV), w.segments, causal=True)
+    torch.cuda.synchronize()
+    og, lg, orf, lrf, heads = _sampled_check(q, k, v, o, lse, 0, 24, 1000 + w.seed,
+                                             must_rows=(0, 2047, 2048, w.nq - 1))
+    assert_parity(og, lg, orf, lrf, torch.bfloat16, rows_heads=heads, what="ring 16k")
+
+
+def test_ulysses_128k_full_size_sampled():
+    """4 heads, d=128, 131072 tokens, causal, one call (the bench launch)."""
+    w = WORKLOADS["ulysses_128k_bf16"]
+    q, k, v = workload_inputs(w)
+    o, lse = emulate.ulysses_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    og, lg, orf, lrf, heads = _sampled_check(q, k, v, o, lse, 0, 48, 1000 + w.seed)
+    assert_parity(og, lg, orf, lrf, torch.bfloat16, rows_heads=heads, what="ulysses 128k")
+
+
+def test_usp_forward_full_size_sampled():
+    """GQA 8/2, d=128, query block 7 of 8 (32768 rows) swept over 8 KV blocks
+    of 32768; 2 heads x 512 sampled rows against the oracle."""
+    w = WORKLOADS["usp_gqa_256k_bf16"]
+    q, k, v = workload_inputs(w)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    emulate.sweep_fwd(q.to(DEV), k.to(DEV), v.to(DEV), w.segments, w.q_block, True, out, lse)
+    torch.cuda.synchronize()
+    blk = w.nk // w.segments
+    rows = []
+    for h in (1, 6):
+        for i in sample_rows(w.nq, 512, 2000 + h, must=(0, w.nq - 1)):
+            rows.append(h * w.nq + i)
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=w.q_block * blk,
+                                   rows=rows)
+    og = to_np(out).reshape(-1, w.d)[rows]
+    lg = to_np(lse).reshape(-1)[rows]
+    assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // w.nq,
+                  what="usp fwd")
