@@ -1,0 +1,73 @@
+"""Host-side logic on the CPU: FLOP accounting, ring schedules, seeded inputs."""
+import itertools
+
+import pytest
+import torch
+
+from bench import visible_pairs
+from long_sequence_exact_amd.emulate import ring_order
+from long_sequence_exact_amd.synth import WORKLOADS, draw, sample_rows
+
+
+def test_visible_pairs_matches_brute_force():
+    for nq, nk, d in itertools.product([0, 1, 5, 17], [0, 1, 4, 19],
+                                       [None, -30, -5, -1, 0, 1, 3, 20, 40]):
+        brute = sum(1 for i in range(nq) for j in range(nk) if d is None or j <= i + d)
+        assert visible_pairs(nq, nk, d) == brute
+
+
+def test_headline_flop_count():
+    # causal 131072 tokens: N(N+1)/2 pairs per head, 4*d flops per pair, 4 heads
+    n = 131072
+    assert visible_pairs(n, n, 0) == n * (n + 1) // 2 == 8_590_000_128
+    assert 4 * 128 * 4 * visible_pairs(n, n, 0) == 17_592_320_262_144
+
+
+def test_ring_schedule_covers_causal_attention_exactly():
+    # 8 ranks x 2048 rows at 16384 tokens: the non-skipped (rank, step) pairs
+    # are 36 and their visible pairs sum to causal attention over 16384 tokens.
+    P, blk = 8, 2048
+    calls, pairs = 0, 0
+    for r in range(P):
+        order = ring_order(r, P)
+        assert sorted(order) == list(range(P)) and order[0] == r
+        for j in order:
+            delta = (r - j) * blk
+            if delta + blk - 1 < 0:
+                continue
+            calls += 1
+            pairs += visible_pairs(blk, blk, delta)
+    assert calls == 36
+    assert pairs == visible_pairs(P * blk, P * blk, 0) == 134_225_920
+
+
+def test_usp_share_pairs():
+    w = WORKLOADS["usp_gqa_256k_bf16"]
+    blk = w.nk // w.segments
+    total = sum(visible_pairs(w.nq, blk, (w.q_block - j) * blk) for j in range(w.segments))
+    assert total == 8_053_080_064
+
+
+def test_draw_is_seeded_and_rounds_to_bf16():
+    a = draw([(3, 5)], 11, torch.bfloat16)[0]
+    b = draw([(3, 5)], 11, torch.bfloat16)[0]
+    f = draw([(3, 5)], 11, torch.float32)[0]
+    assert torch.equal(a, b)
+    assert torch.equal(a, f.to(torch.bfloat16))
+
+
+def test_sample_rows():
+    r = sample_rows(1000, 20, 3, must=(0, -1))
+    assert len(r) == 20 and 0 in r and 999 in r and r == sorted(set(r))
+    assert sample_rows(1000, 20, 3, must=(0, -1)) == r
+    assert sample_rows(5, 20, 1) == [0, 1, 2, 3, 4]
+
+
+def test_bench_refuses_multi_gpu():
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert p.returncode == 2 and "one GPU" in p.stdout
