@@ -10,8 +10,9 @@
 // kernels ("LongNet ...", Results); the tiling below is designed for gfx950.
 //
 // Work decomposition
-//   * one workgroup = 4 waves = 128 query rows of one (batch, segment, head);
-//     each wave owns 32 query rows for the whole kernel;
+//   * one workgroup = 8 waves = 256 query rows of one (batch, segment, head);
+//     each wave owns 32 query rows for the whole kernel; two waves share a
+//     SIMD, so one wave's softmax VALU work overlaps the other's MFMAs;
 //   * the workgroup walks the KV segment in tiles of BK keys (64 for d=128,
 //     128 for d=64), staged HBM -> VGPR -> LDS; the next tile's global loads
 //     are issued before the current tile is computed;
@@ -20,6 +21,10 @@
 //     accumulator puts one query row in one lane column: the row max needs a
 //     single cross-lane step (lane l <-> l^32) and the row sum none until the
 //     epilogue;
+//   * the reference max of a row is only raised when new scores exceed it by
+//     more than 2^8 (a conditional rescale): the exponentials stay <= 256,
+//     which fp32 and bf16 hold with full relative precision, and the O
+//     rescale is skipped for most tiles;
 //   * P^T is rounded to bf16 in registers and is directly the B operand of
 //     O^T += V^T P^T; V is transposed while it is written to LDS, in a key
 //     order that matches the accumulator's row interleave;
@@ -39,11 +44,12 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kBQ = 32 * kWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;  // log2 headroom before the max is raised
 
 template <int D>
 struct Cfg {
@@ -52,7 +58,8 @@ struct Cfg {
     static constexpr int VSTR = BK + 8;               // V^T row pitch in LDS (bf16)
     static constexpr int KCH = BK * D / 8 / kThreads; // 16-byte K chunks per thread
     static constexpr int VG = BK / 4;                 // 4-key groups per tile
-    static_assert(VG * (D / 8) == kThreads, "one 4x8 V block per thread");
+    static constexpr int VBLK = VG * (D / 8);        // 4x8 V blocks per tile
+    static_assert(VBLK <= kThreads && BK * D / 8 == KCH * kThreads, "staging split");
 };
 
 __device__ inline unsigned pack_bf16(float a, float b)
@@ -136,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 
     u32x4 kreg[C::KCH];
     u32x4 vreg[4];
-    const int vkg = tid % C::VG, vdc = tid / C::VG;
+    const bool vthread = tid < C::VBLK;  // threads 0..VBLK-1 also stage one V block
+    const int vkg = tid % C::VG, vdc = (tid / C::VG) % (D / 8);
 
     auto load_tile = [&](int t) {
         const int j0 = t * BK;
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
         for (int u = 0; u < 4; ++u) {
             const int j = j0 + vkg * 4 + u;
             u32x4 z = {0u, 0u, 0u, 0u};
-            vreg[u] = (j < p.Nk) ? *(const u32x4 *)(V + (int64_t)j * p.v.sn + vdc * 8) : z;
+            vreg[u] = (vthread && j < p.Nk) ? *(const u32x4 *)(V + (int64_t)j * p.v.sn + vdc * 8) : z;
         }
     };
 
@@ -164,6 +172,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
             *(u32x4 *)(&Ks[row * C::KSTR + col]) = kreg[u];
         }
         // 4 keys x 8 d block -> 8 rows of V^T, 4 keys (8 bytes) each
+        if (!vthread)
+            return;
         const int pos = vt_pos(vkg);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -229,9 +239,26 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
             for (int e = 0; e < 16; ++e)
                 mx = fmaxf(mx, sacc[kb][e]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+
+        // conditional rescale: raise the reference max only when some score
+        // exceeds it by more than the slack (always on a row's first keys)
+        const float mxc = mx * c;
+        const bool upd = mxc > m_run + kRescaleSlack;
+        const bool any_upd = __any(upd);
+        float alpha = 1.f;
+        if (any_upd) {
+            const float m_new = upd ? mxc : m_run;
+            // exp2(-inf) = 0 for a row's first visible keys; rows that keep
+            // their max (fully masked ones included) keep alpha = 1
+            alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            m_run = m_new;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[i][e] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
         unsigned pk[BK / 32][8];
         float lsum = 0.f;
@@ -245,12 +272,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
                 pk[kb][e >> 1] = pack_bf16(p0, p1);
             }
         l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                oacc[i][e] *= alpha;
 
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
