@@ -186,6 +186,17 @@ int check_out(const seqattn_tensor *o, const seqattn_tensor *lse, const seqattn_
 
 hipStream_t stream_of(void *s) { return (hipStream_t)s; }
 
+// The bf16 forward addresses one head's rows with 32-bit byte offsets
+// (buffer loads, which also zero-fill rows past the end): each head's rows,
+// plus the tile overrun of the last tile, must span less than 2 GiB.
+int check_head_extent(const seqattn_tensor *t, const char *name, int64_t row_step)
+{
+    const int64_t rows = t->n + 512 * row_step;
+    if (rows * t->stride_n * esize(t->dtype) >= ((int64_t)1 << 31))
+        return fail(SEQATTN_ERR_UNSUPPORTED, "%s: one head spans >= 2 GiB", name);
+    return SEQATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,6 +234,10 @@ int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
     const bool acc = flags & SEQATTN_ACCUMULATE;
     if ((acc || q->dtype == SEQATTN_F32) && o->dtype != SEQATTN_F32)
         return fail(SEQATTN_ERR_DTYPE, "o must be fp32 (accumulate or fp32 inputs)");
+    if (q->dtype == SEQATTN_BF16 &&
+        ((st = check_head_extent(q, "q", 1)) || (st = check_head_extent(k, "k", 1)) ||
+         (st = check_head_extent(v, "v", 1))))
+        return st;
 
     FwdParams p;
     p.q = view_of(q);
@@ -332,6 +347,12 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
         if (segment_lengths[i] < 1 || dilations[i] < 1 || segment_lengths[i] >= kMaxRows ||
             dilations[i] >= kMaxRows)
             return fail(SEQATTN_ERR_SHAPE, "branch %d: w and r must be >= 1", i);
+    int64_t rmax = 1;
+    for (int i = 0; i < n_branches; ++i)
+        rmax = std::max<int64_t>(rmax, dilations[i]);
+    if ((st = check_head_extent(q, "q", rmax)) || (st = check_head_extent(k, "k", rmax)) ||
+        (st = check_head_extent(v, "v", rmax)))
+        return st;
     const bool o_bf16 = o->dtype == SEQATTN_BF16;
     const size_t need = seqattn_workspace_size(SEQATTN_OP_DILATED_FWD, q, o, n_branches);
     if (need > 0) {

@@ -45,39 +45,61 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
 constexpr int kWaves = 8;
-constexpr int kBQ = 32 * kWaves;
+constexpr int kBQ = 32 * kWaves;      // query rows per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 headroom before the max is raised
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 template <int D>
 struct Cfg {
     static constexpr int BK = (D == 128) ? 64 : 128;  // keys per tile
-    static constexpr int KSTR = D + 8;                // K row pitch in LDS (bf16)
-    static constexpr int VSTR = BK + 8;               // V^T row pitch in LDS (bf16)
-    static constexpr int KCH = BK * D / 8 / kThreads; // 16-byte K chunks per thread
-    static constexpr int VG = BK / 4;                 // 4-key groups per tile
-    static constexpr int VBLK = VG * (D / 8);        // 4x8 V blocks per tile
-    static_assert(VBLK <= kThreads && BK * D / 8 == KCH * kThreads, "staging split");
+    // LDS row pitches (bf16 elements).  K: +8 so the 32 rows an MFMA operand
+    // read touches fall in distinct banks.  V: a pitch of 16 (mod 64) dwords,
+    // so the four rows x 32 bytes each 16-lane group of a transposing read
+    // touches, and the neighbouring group's, cover all 64 banks once.
+    static constexpr int KSTR = D + 8;
+    static constexpr int VSTR = D + 32;
+    static constexpr int CH = BK * D / 8;             // 16-byte chunks per tile
+    static constexpr int CPT = CH / kThreads;         // chunks per thread (K and V each)
+    static_assert(CPT * kThreads == CH, "tile split");
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline unsigned pack_bf16(float a, float b)
 {
-    // round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950)
-    bf16 x = (bf16)a, y = (bf16)b;
-    return (unsigned)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+    // two floats -> two bf16, round-to-nearest-even, one v_cvt_pk_bf16_f32
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
-// Position of key group (4 keys starting at 4*kg) inside the permuted V^T row:
-// within every 16 keys the order is [0-3, 8-11, 4-7, 12-15], so that lane half
-// 0 of the PV MFMA reads keys {0-3, 8-11} and half 1 keys {4-7, 12-15} as one
-// 16-byte chunk -- the same keys the S^T accumulator gives each lane half.
-__device__ inline int vt_pos(int kg)
+// Buffer resource over `bytes` bytes at p: loads past the end return zeros,
+// which is how rows beyond a segment's end are padded without branches.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes)
 {
-    const int q4 = kg & 3;
-    return (kg >> 2) * 16 + (((q4 & 1) << 1) | (q4 >> 1)) * 4;
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, kRsrcWord3);
+}
+
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Four bf16 of a transposing LDS read (ds_read_b64_tr_b16): within each group
+// of 16 lanes, lane l receives element l%4 of the 8-byte vectors addressed by
+// lanes 4e + (l%16)/4, e = 0..3, of its group.
+__device__ inline v4i16 read_tr(const bf16 *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)((__attribute__((address_space(3))) char *)(
+            (__attribute__((address_space(3))) bf16 *)p)));
 }
 
 template <int D>
@@ -86,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     using C = Cfg<D>;
     constexpr int BK = C::BK;
     __shared__ __attribute__((aligned(16))) bf16 Ks[BK * C::KSTR];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::VSTR];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[BK * C::VSTR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -104,6 +126,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh;
     const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh;
     const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh;
+    // valid bytes of each view: rows past Nq / Nk read as zeros
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, p.Nq > 0 ? ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2 : 0);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, p.Nk > 0 ? ((int64_t)(p.Nk - 1) * p.k.sn + D) * 2 : 0);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, p.Nk > 0 ? ((int64_t)(p.Nk - 1) * p.v.sn + D) * 2 : 0);
 
     const int q0 = qt * kBQ;
     const int q0w = q0 + wave * 32;
@@ -120,15 +146,11 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
         return;  // empty partial: the running accumulator is unchanged
 
     // Q tile as the B operand of S^T = K Q^T: lane (l32, hl) holds row qrow,
-    // d = 16*kk + 8*hl .. +8.
+    // d = 16*kk + 8*hl .. +8 (rows past Nq read as zeros).
     bf16x8 qf[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qrow < p.Nq)
-            raw = *(const u32x4 *)(Q + (int64_t)qrow * p.q.sn + kk * 16 + hl * 8);
-        qf[kk] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = __builtin_bit_cast(bf16x8, load16(qr, (qrow * (int)p.q.sn + kk * 16 + hl * 8) * 2));
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -137,56 +159,43 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
         for (int e = 0; e < 16; ++e)
             oacc[i][e] = 0.f;
 
-    float m_run = -INFINITY;  // running max, in units of log2
+    float m_run = -INFINITY;  // running reference max, in units of log2
     float l_run = 0.f;        // this lane's partial row sum
     const float c = p.scale * kLog2e;
 
-    u32x4 kreg[C::KCH];
-    u32x4 vreg[4];
-    const bool vthread = tid < C::VBLK;  // threads 0..VBLK-1 also stage one V block
-    const int vkg = tid % C::VG, vdc = (tid / C::VG) % (D / 8);
-
+    // staging: thread tid moves 16-byte chunks tid + u*kThreads of the K and
+    // the V tile (row = chunk / (D/8), column = 8 * (chunk % (D/8)))
+    u32x4 kreg[C::CPT], vreg[C::CPT];
+    int srow[C::CPT], scol[C::CPT];
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+        const int ch = tid + u * kThreads;
+        srow[u] = ch / (D / 8);
+        scol[u] = (ch % (D / 8)) * 8;
+    }
     auto load_tile = [&](int t) {
         const int j0 = t * BK;
 #pragma unroll
-        for (int u = 0; u < C::KCH; ++u) {
-            const int ch = tid + u * kThreads;
-            const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-            const int j = j0 + row;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kreg[u] = (j < p.Nk) ? *(const u32x4 *)(K + (int64_t)j * p.k.sn + col) : z;
+        for (int u = 0; u < C::CPT; ++u) {
+            kreg[u] = load16(kr, ((j0 + srow[u]) * (int)p.k.sn + scol[u]) * 2);
+            vreg[u] = load16(vr, ((j0 + srow[u]) * (int)p.v.sn + scol[u]) * 2);
         }
+    };
+    auto store_tile = [&]() {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + vkg * 4 + u;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            vreg[u] = (vthread && j < p.Nk) ? *(const u32x4 *)(V + (int64_t)j * p.v.sn + vdc * 8) : z;
+        for (int u = 0; u < C::CPT; ++u) {
+            *(u32x4 *)(&Ks[srow[u] * C::KSTR + scol[u]]) = kreg[u];
+            *(u32x4 *)(&Vs[srow[u] * C::VSTR + scol[u]]) = vreg[u];
         }
     };
 
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int u = 0; u < C::KCH; ++u) {
-            const int ch = tid + u * kThreads;
-            const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-            *(u32x4 *)(&Ks[row * C::KSTR + col]) = kreg[u];
-        }
-        // 4 keys x 8 d block -> 8 rows of V^T, 4 keys (8 bytes) each
-        if (!vthread)
-            return;
-        const int pos = vt_pos(vkg);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const unsigned a0 = vreg[0][m], a1 = vreg[1][m], a2 = vreg[2][m], a3 = vreg[3][m];
-            uint2 lo, hi;
-            lo.x = (a0 & 0xffffu) | (a1 << 16);
-            lo.y = (a2 & 0xffffu) | (a3 << 16);
-            hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
-            hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
-            *(uint2 *)(&Vt[(vdc * 8 + 2 * m) * C::VSTR + pos]) = lo;
-            *(uint2 *)(&Vt[(vdc * 8 + 2 * m + 1) * C::VSTR + pos]) = hi;
-        }
-    };
+    // transposing-read addresses of the PV A operand (V^T, rows d, k = keys):
+    // read r of k-slice ks, d-block i: lane (group gg = lane/16, i' = lane%16)
+    // addresses V[16ks + 8r + 4(gg/2) + i'/4][32i + 16(gg%2) + 4(i'%4)], so
+    // lane l receives V[16ks + 8r + 4hl + e][32i + l32], e = 0..3 -- the key
+    // order of the P^T accumulator rows.
+    const int gg = lane >> 4, ip = lane & 15;
+    const int vt_off = (4 * (gg >> 1) + (ip >> 2)) * C::VSTR + 16 * (gg & 1) + 4 * (ip & 3);
 
     if (ntiles > 0)
         load_tile(0);
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
             load_tile(t + 1);
 
         const int j0 = t * BK;
-        // whole tile invisible to this wave's rows (causal diagonal): skip
+        // whole tile in this wave's causal future: nothing to compute
         if (!p.noncausal && j0 > q0w + 31 + p.delta)
             continue;
 
@@ -281,7 +290,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const bf16x8 a = *(const bf16x8 *)(&Vt[(i * 32 + l32) * C::VSTR + ks * 16 + hl * 8]);
+                const bf16 *base = &Vs[(16 * ks) * C::VSTR + 32 * i + vt_off];
+                const v4i16 lo = read_tr(base);
+                const v4i16 hi = read_tr(base + 8 * C::VSTR);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
             }
         }
