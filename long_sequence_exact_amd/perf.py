@@ -1,0 +1,130 @@
+"""Per-workload timing of the HIP path (one JSON line per workload).
+
+    python -m long_sequence_exact_amd.perf [--workload NAME ...] [--reps R]
+
+For each synthetic workload the whole hot path is timed with HIP events on
+the launch stream, inputs already resident in HBM:
+  ring_16k_bf16       8 ranks x 8 KV segments, fused-merge ring sweep
+  ulysses_128k_bf16   one causal forward launch (the benchmark's step)
+  longnet_32k_bf16    dilated attention, 5 branches merged by LSE
+  usp_gqa_256k_bf16   forward sweep over 8 KV blocks, then backward sweep
+  lse_merge           standalone merge of two [32, 16384, 128] partials
+                      (fp32 accumulator + bf16 partial), reported in GB/s
+FLOPs are algorithmic (4*d per visible pair forward, 10*d backward); bytes
+for the merge are the tensors read and written.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+
+import torch
+
+from . import attn_segment_bwd, dilated_attn_fwd, emulate, lse_merge
+from .synth import WORKLOADS, draw, workload_inputs
+
+PEAK_TFLOPS = 2500.0
+PEAK_GBS = 8000.0
+
+
+def pairs(nq, nk, delta):
+    """Visible (query, key) pairs with key j visible to query i iff j <= i + delta."""
+    if delta is None:
+        return nq * nk
+    tot = 0
+    lo = max(0, -delta - 1)
+    hi = min(nq, max(0, nk - delta - 1))
+    if hi > lo:
+        a, b = lo + delta + 1, hi + delta
+        tot += (a + b) * (hi - lo) // 2
+    tot += max(0, nq - max(lo, hi)) * nk
+    return tot
+
+
+def timed(fn, reps, warmup=2):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def run(name, reps):
+    dev = "cuda"
+    if name == "lse_merge":
+        H, N, d = 32, 16384, 128
+        oa, ob = draw([(1, H, N, d), (1, H, N, d)], 11, torch.float32)
+        la, lb = draw([(1, H, N), (1, H, N)], 12, torch.float32)
+        oa, la, lb = oa.to(dev), la.to(dev), lb.to(dev)
+        ob = ob.to(torch.bfloat16).to(dev)
+        ms = timed(lambda: lse_merge(oa, la, ob, lb), reps)
+        nbytes = oa.numel() * 4 * 2 + ob.numel() * 2 + la.numel() * 4 * 2 + lb.numel() * 4
+        return {"workload": name, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_GBS, 3), "bytes": nbytes}
+    w = WORKLOADS[name]
+    if name == "ring_16k_bf16":
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        ms = timed(lambda: emulate.ring_fwd(q, k, v, w.segments, causal=True), reps)
+        fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
+    elif name == "ulysses_128k_bf16":
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        from . import attn_segment_fwd
+        ms = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=0, out=out, lse=lse), reps)
+        fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
+    elif name == "longnet_32k_bf16":
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        ms = timed(lambda: dilated_attn_fwd(q, k, v, w.segment_lengths, w.dilations,
+                                            out=out, lse=lse), reps)
+        npairs = sum((w.nq // sl) * (sl // r) ** 2
+                     for sl, r in zip(w.segment_lengths, w.dilations))
+        fl = 4.0 * w.d * w.hq * npairs
+    elif name == "usp_gqa_256k_bf16":
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
+        blk = w.nk // w.segments
+        npairs = sum(pairs(w.nq, blk, (w.q_block - j) * blk) for j in range(w.segments))
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        ms_f = timed(lambda: emulate.sweep_fwd(q, k, v, w.segments, w.q_block, True, out, lse),
+                     reps)
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        ms_b = timed(lambda: emulate.usp_bwd(q, k, v, out, lse, do, w.segments, w.q_block,
+                                             True, dq=dq, dk=dk, dv=dv), reps)
+        fl_f = 4.0 * w.d * w.hq * npairs
+        fl_b = 10.0 * w.d * w.hq * npairs
+        return {"workload": name, "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
+                "fwd_TFLOP/s": round(fl_f / ms_f / 1e9, 1),
+                "bwd_TFLOP/s": round(fl_b / ms_b / 1e9, 1),
+                "fwd_frac_peak": round(fl_f / ms_f / 1e9 / PEAK_TFLOPS, 3),
+                "bwd_frac_peak": round(fl_b / ms_b / 1e9 / PEAK_TFLOPS, 3)}
+    else:
+        raise ValueError(name)
+    return {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
+            "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", nargs="*",
+                    default=["ulysses_128k_bf16", "ring_16k_bf16", "longnet_32k_bf16",
+                             "usp_gqa_256k_bf16", "lse_merge"])
+    ap.add_argument("--reps", type=int, default=5)
+    args = ap.parse_args()
+    for name in args.workload:
+        print(json.dumps(run(name, args.reps)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
