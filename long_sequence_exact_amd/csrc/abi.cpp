@@ -449,6 +449,8 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         return fail(SEQATTN_ERR_UNSUPPORTED, "backward takes bf16 q/k/v");
     if (d_o->dtype != SEQATTN_BF16)
         return fail(SEQATTN_ERR_DTYPE, "d_o must be bf16");
+    if ((st = check_head_extent(q, "q", 1)) || (st = check_head_extent(d_o, "d_o", 1)))
+        return st;
     if (dq->dtype != SEQATTN_F32)
         return fail(SEQATTN_ERR_DTYPE, "dq must be fp32 (accumulated)");
     if (flags != 0)

@@ -13,13 +13,17 @@
 //   * bwd_main: one workgroup = 4 waves = 128 keys of one (batch, KV head);
 //     each wave keeps its 32 keys' K and V rows in VGPRs and its dK^T, dV^T
 //     accumulators (fp32) for the whole kernel, and loops over the query
-//     heads sharing the KV head and over the visible 64-row query tiles.
+//     heads sharing the KV head and over the visible 64-row query tiles; the
+//     next tile's Q, dO rows, LSE and D are loaded into VGPRs (range-checked
+//     buffer loads) while the current tile is computed.
 //     Per tile the scores are recomputed as S = Q K^T with keys in lane
 //     columns (v_mfma_f32_32x32x16_bf16), so P and dS are directly the B
-//     operands of dV^T += dO^T P and dK^T += Q^T dS; Q^T and dO^T are staged
-//     transposed in LDS in the matching row interleave.  dS goes through LDS
-//     once more for dQ = dS K (K^T staged in LDS once per workgroup), which
-//     is added to the fp32 dQ with hardware float atomics.
+//     operands of dV^T += dO^T P and dK^T += Q^T dS; the Q^T and dO^T A
+//     operands are read from the row-major Q / dO tiles in LDS with
+//     transposing reads (ds_read_b64_tr_b16).  dS^T goes to LDS (8-byte rows
+//     per lane) and is read back transposed as the A operand of dQ = dS K
+//     (K^T staged in LDS once per workgroup); dQ is added to the fp32 output
+//     with hardware float atomics.
 #include "common.h"
 
 namespace seqattn {
@@ -36,19 +40,14 @@ constexpr int kBKV = 32 * kWaves;  // keys per workgroup
 constexpr int kBQ = 64;            // query rows per iteration
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 __device__ inline unsigned pack_bf16(float a, float b)
 {
-    bf16 x = (bf16)a, y = (bf16)b;
-    return (unsigned)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
-}
-
-// Same 16-row interleave as the forward's V^T: within 16 rows the order is
-// [0-3, 8-11, 4-7, 12-15] (matches the accumulator rows each lane half holds).
-__device__ inline int perm_pos(int g4)
-{
-    const int q4 = g4 & 3;
-    return (g4 >> 2) * 16 + (((q4 & 1) << 1) | (q4 >> 1)) * 4;
+    // two floats -> two bf16, round-to-nearest-even, one v_cvt_pk_bf16_f32
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
 __device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -91,12 +90,41 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
 
 template <int D>
 struct BCfg {
-    static constexpr int QSTR = D + 8;        // Q / dO row pitch (bf16)
-    static constexpr int TSTR = kBQ + 8;      // Q^T / dO^T row pitch
-    static constexpr int SSTR = kBKV + 8;     // dS row pitch
-    static constexpr int KTSTR = kBKV + 8;    // K^T row pitch
-    static constexpr int QBLK = (kBQ / 4) * (D / 8);  // 4x8 blocks per Q tile
+    static constexpr int QSTR = D + 8;         // Q / dO row pitch (bf16)
+    static constexpr int KTSTR = kBKV + 8;     // K^T row pitch
+    static constexpr int DSTR = kBQ + 4;       // dS^T row pitch (rows 8-byte aligned)
+    static constexpr int CPT = kBQ * D / 8 / kThreads;  // 16-byte chunks per thread per tile
+    static_assert(CPT * kThreads * 8 == kBQ * D, "tile split");
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes)
+{
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, kRsrcWord3);
+}
+
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane l receives element l%4
+// of the 8-byte vectors addressed by lanes 4e + (l%16)/4, e = 0..3.
+__device__ inline v4i16 read_tr(const bf16 *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)((__attribute__((address_space(3))) char *)(
+            (__attribute__((address_space(3))) bf16 *)p)));
+}
+
+__device__ inline bf16x8 cat_tr(v4i16 lo, v4i16 hi)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
@@ -104,16 +132,15 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     using C = BCfg<D>;
     __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * C::QSTR];
     __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * C::QSTR];
-    __shared__ __attribute__((aligned(16))) bf16 QTs[D * C::TSTR];
-    __shared__ __attribute__((aligned(16))) bf16 dOTs[D * C::TSTR];
-    __shared__ __attribute__((aligned(16))) bf16 dSs[kBQ * C::SSTR];
     __shared__ __attribute__((aligned(16))) bf16 KTs[D * C::KTSTR];
+    __shared__ __attribute__((aligned(16))) bf16 dSTs[kBKV * C::DSTR];
     __shared__ float lse2s[kBQ];
     __shared__ float Dsh[kBQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hl = lane >> 5;
+    const int gg = lane >> 4, ip = lane & 15;
 
     const int nkt = (p.Nk + kBKV - 1) / kBKV;
     const int kt = (int)(blockIdx.x % nkt);
@@ -181,158 +208,163 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         const int first_q = max(0, k0 - p.delta);  // smallest query seeing key k0
         qt_begin = min(nqt, first_q / kBQ);
     }
+    const int per_head = nqt - qt_begin;
+    const int niters = group * per_head;
 
-    for (int hh = 0; hh < group; ++hh) {
-        const int h = g * group + hh;
+    // staging of the (query head, query tile) of iteration `it` into VGPRs
+    u32x4 qreg[C::CPT], oreg[C::CPT];
+    float lreg = 0.f, dreg = 0.f;
+    int srow[C::CPT], scol[C::CPT];
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+        const int ch = tid + u * kThreads;
+        srow[u] = ch / (D / 8);
+        scol[u] = (ch % (D / 8)) * 8;
+    }
+    auto prefetch = [&](int it) {
+        const int h = g * group + it / per_head;
+        const int q0 = (qt_begin + it % per_head) * kBQ;
         const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + h * p.q.sh;
         const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh;
-        const float *LSE = (const float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh;
-        const float *Dv = p.dvec + ((int64_t)b * p.Hq + h) * p.Nq;
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2);
+        const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(p.Nq - 1) * p.dout.sn + D) * 2);
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            qreg[u] = load16(qr, ((q0 + srow[u]) * (int)p.q.sn + scol[u]) * 2);
+            oreg[u] = load16(orr, ((q0 + srow[u]) * (int)p.dout.sn + scol[u]) * 2);
+        }
+        if (tid < kBQ) {
+            const int i = q0 + tid;
+            lreg = INFINITY;  // +inf: the row contributes P = 0
+            dreg = 0.f;
+            if (i < p.Nq) {
+                const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh +
+                                   (int64_t)i * p.lse.sn);
+                if (lv != -INFINITY)
+                    lreg = lv * kLog2e;
+                dreg = p.dvec[((int64_t)b * p.Hq + h) * p.Nq + i];
+            }
+        }
+    };
+
+    // transposing-read offsets (see read_tr): P/dS B-operand order for the
+    // Q^T / dO^T operands, natural key order for the dS operand of dQ
+    const int tq_off = (4 * (gg >> 1) + (ip >> 2)) * C::QSTR + 16 * (gg & 1) + 4 * (ip & 3);
+    const int ts_off = (8 * (gg >> 1) + (ip >> 2)) * C::DSTR + 16 * (gg & 1) + 4 * (ip & 3);
+
+    if (niters > 0)
+        prefetch(0);
+
+    for (int it = 0; it < niters; ++it) {
+        const int h = g * group + it / per_head;
+        const int q0 = (qt_begin + it % per_head) * kBQ;
         float *dQ = (float *)p.dq.ptr + b * p.dq.sb + h * p.dq.sh;
 
-        for (int qt = qt_begin; qt < nqt; ++qt) {
-            const int q0 = qt * kBQ;
-            __syncthreads();
-            // ---- stage Q, dO tiles (row-major and transposed/interleaved) ----
-            for (int job = tid; job < 2 * C::QBLK; job += kThreads) {
-                const bool isq = job < C::QBLK;
-                const int blk = isq ? job : job - C::QBLK;
-                const int qg = blk % (kBQ / 4), dc = blk / (kBQ / 4);
-                const bf16 *src = isq ? Q : dO;
-                const int64_t sn = isq ? p.q.sn : p.dout.sn;
-                bf16 *rm = isq ? Qs : dOs;
-                bf16 *tr = isq ? QTs : dOTs;
-                unsigned a[4][4];
+        __syncthreads();  // previous iteration done with Qs, dOs, dSTs
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            *(u32x4 *)(&Qs[srow[u] * C::QSTR + scol[u]]) = qreg[u];
+            *(u32x4 *)(&dOs[srow[u] * C::QSTR + scol[u]]) = oreg[u];
+        }
+        if (tid < kBQ) {
+            lse2s[tid] = lreg;
+            Dsh[tid] = dreg;
+        }
+        __syncthreads();
+        if (it + 1 < niters)
+            prefetch(it + 1);
+
+        // ---- S = Q K^T, dP = dO V^T for 2 blocks of 32 queries ----
+        const bool need_mask = (k0 + kBKV > p.Nk) || (q0 + kBQ > p.Nq) ||
+                               (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
+        unsigned pP[2][8], pS[2][8];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            f32x16 s, dp;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                s[e] = dp[e] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const bf16x8 aq = *(const bf16x8 *)(&Qs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                const bf16x8 ad = *(const bf16x8 *)(&dOs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
+            }
+            // element e: query row qb*32 + 8(e/4) + 4hl + e%4 of the tile
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int r0 = qb * 32 + gq * 8 + hl * 4;
+                const float4 l2 = *(const float4 *)(&lse2s[r0]);
+                const float4 dd = *(const float4 *)(&Dsh[r0]);
+                const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+                const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
+                float pv[4], sv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int i = q0 + qg * 4 + u;
-                    u32x4 x = {0u, 0u, 0u, 0u};
-                    if (i < p.Nq)
-                        x = *(const u32x4 *)(src + (int64_t)i * sn + dc * 8);
-                    *(u32x4 *)(&rm[(qg * 4 + u) * C::QSTR + dc * 8]) = x;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        a[u][m] = x[m];
-                }
-                const int pos = perm_pos(qg);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    uint2 lo, hi;
-                    lo.x = (a[0][m] & 0xffffu) | (a[1][m] << 16);
-                    lo.y = (a[2][m] & 0xffffu) | (a[3][m] << 16);
-                    hi.x = (a[0][m] >> 16) | (a[1][m] & 0xffff0000u);
-                    hi.y = (a[2][m] >> 16) | (a[3][m] & 0xffff0000u);
-                    *(uint2 *)(&tr[(dc * 8 + 2 * m) * C::TSTR + pos]) = lo;
-                    *(uint2 *)(&tr[(dc * 8 + 2 * m + 1) * C::TSTR + pos]) = hi;
-                }
-            }
-            if (tid < kBQ) {
-                const int i = q0 + tid;
-                float l2 = INFINITY, dd = 0.f;  // +inf: row contributes P = 0
-                if (i < p.Nq) {
-                    const float lv = LSE[(int64_t)i * p.lse.sn];
-                    if (lv != -INFINITY)
-                        l2 = lv * kLog2e;
-                    dd = Dv[i];
-                }
-                lse2s[tid] = l2;
-                Dsh[tid] = dd;
-            }
-            __syncthreads();
-
-            // ---- S = Q K^T, dP = dO V^T for 2 blocks of 32 queries ----
-            const bool need_mask = (k0 + kBKV > p.Nk) || (q0 + kBQ > p.Nq) ||
-                                   (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
-            unsigned pP[2][8], pS[2][8];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                f32x16 s, dp;
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    s[e] = dp[e] = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const bf16x8 aq = *(const bf16x8 *)(&Qs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
-                    const bf16x8 ad = *(const bf16x8 *)(&dOs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
-                }
-                // element e: query row qb*32 + 8(e/4) + 4hl + e%4 of the tile
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int r0 = qb * 32 + gq * 8 + hl * 4;
-                    const float4 l2 = *(const float4 *)(&lse2s[r0]);
-                    const float4 dd = *(const float4 *)(&Dsh[r0]);
-                    const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-                    const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
-                    float pv[4], sv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int e = gq * 4 + u;
-                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
-                        if (need_mask) {
-                            const int qi = q0 + r0 + u;
-                            const bool vis = key < p.Nk && qi < p.Nq &&
-                                             (p.noncausal || key - qi <= p.delta);
-                            pe = vis ? pe : 0.f;
-                        }
-                        pv[u] = pe;
-                        sv[u] = pe * (dp[e] - dv[u]);
+                    const int e = gq * 4 + u;
+                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
+                    if (need_mask) {
+                        const int qi = q0 + r0 + u;
+                        const bool vis = key < p.Nk && qi < p.Nq &&
+                                         (p.noncausal || key - qi <= p.delta);
+                        pe = vis ? pe : 0.f;
                     }
-                    pP[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
-                    pP[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
-                    pS[qb][gq * 2 + 0] = pack_bf16(sv[0], sv[1]);
-                    pS[qb][gq * 2 + 1] = pack_bf16(sv[2], sv[3]);
-                    // dS to LDS, [query][key] (natural order) for dQ
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const bf16 x = (bf16)sv[u];
-                        dSs[(r0 + u) * C::SSTR + wave * 32 + l32] = x;
-                    }
+                    pv[u] = pe;
+                    sv[u] = pe * (dp[e] - dv[u]);
                 }
+                pP[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
+                pP[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
+                pS[qb][gq * 2 + 0] = pack_bf16(sv[0], sv[1]);
+                pS[qb][gq * 2 + 1] = pack_bf16(sv[2], sv[3]);
+                // dS^T row `key`, 4 consecutive queries (8 bytes)
+                uint2 w = {pS[qb][gq * 2 + 0], pS[qb][gq * 2 + 1]};
+                *(uint2 *)(&dSTs[(wave * 32 + l32) * C::DSTR + r0]) = w;
             }
+        }
 
-            // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 64 query rows) ----
+        // ---- dV^T += dO^T P, dK^T += Q^T dS (k = the tile's 64 query rows) ----
 #pragma unroll
-            for (int ks = 0; ks < kBQ / 16; ++ks) {
-                const int qb = ks >> 1, half = ks & 1;
-                u32x4 wp = {pP[qb][half * 4 + 0], pP[qb][half * 4 + 1], pP[qb][half * 4 + 2],
-                            pP[qb][half * 4 + 3]};
-                u32x4 ws = {pS[qb][half * 4 + 0], pS[qb][half * 4 + 1], pS[qb][half * 4 + 2],
-                            pS[qb][half * 4 + 3]};
-                const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
-                const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
+        for (int ks = 0; ks < kBQ / 16; ++ks) {
+            const int qb = ks >> 1, half = ks & 1;
+            u32x4 wp = {pP[qb][half * 4 + 0], pP[qb][half * 4 + 1], pP[qb][half * 4 + 2],
+                        pP[qb][half * 4 + 3]};
+            u32x4 ws = {pS[qb][half * 4 + 0], pS[qb][half * 4 + 1], pS[qb][half * 4 + 2],
+                        pS[qb][half * 4 + 3]};
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
+            const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
 #pragma unroll
-                for (int i = 0; i < D / 32; ++i) {
-                    const bf16x8 ad = *(const bf16x8 *)(&dOTs[(i * 32 + l32) * C::TSTR + ks * 16 + hl * 8]);
-                    const bf16x8 aq = *(const bf16x8 *)(&QTs[(i * 32 + l32) * C::TSTR + ks * 16 + hl * 8]);
-                    dVacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bp, dVacc[i], 0, 0, 0);
-                    dKacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bs, dKacc[i], 0, 0, 0);
-                }
+            for (int i = 0; i < D / 32; ++i) {
+                const int off = (16 * ks) * C::QSTR + 32 * i + tq_off;
+                const bf16x8 ad = cat_tr(read_tr(&dOs[off]), read_tr(&dOs[off + 8 * C::QSTR]));
+                const bf16x8 aq = cat_tr(read_tr(&Qs[off]), read_tr(&Qs[off + 8 * C::QSTR]));
+                dVacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bp, dVacc[i], 0, 0, 0);
+                dKacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bs, dKacc[i], 0, 0, 0);
             }
-            __syncthreads();
+        }
+        __syncthreads();  // dS^T of all 128 keys is in LDS
 
-            // ---- dQ[q][d] += sigma * sum_key dS[q][key] K[key][d] ----
-            constexpr int nblk = (kBQ / 32) * (D / 32);
-            for (int ob = wave; ob < nblk; ob += kWaves) {
-                const int qb = ob % (kBQ / 32), db = ob / (kBQ / 32);
-                f32x16 acc;
+        // ---- dQ[q][d] += sigma * sum_key dS[q][key] K[key][d] ----
+        constexpr int nblk = (kBQ / 32) * (D / 32);
+        for (int ob = wave; ob < nblk; ob += kWaves) {
+            const int qb = ob % (kBQ / 32), db = ob / (kBQ / 32);
+            f32x16 acc;
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[e] = 0.f;
+            for (int e = 0; e < 16; ++e)
+                acc[e] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < kBKV / 16; ++ks) {
-                    const bf16x8 a = *(const bf16x8 *)(&dSs[(qb * 32 + l32) * C::SSTR + ks * 16 + hl * 8]);
-                    const bf16x8 bk = *(const bf16x8 *)(&KTs[(db * 32 + l32) * C::KTSTR + ks * 16 + hl * 8]);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, acc, 0, 0, 0);
-                }
-                const int dcol = db * 32 + l32;
+            for (int ks = 0; ks < kBKV / 16; ++ks) {
+                const int off = (16 * ks) * C::DSTR + 32 * qb + ts_off;
+                const bf16x8 a = cat_tr(read_tr(&dSTs[off]), read_tr(&dSTs[off + 4 * C::DSTR]));
+                const bf16x8 bk = *(const bf16x8 *)(&KTs[(db * 32 + l32) * C::KTSTR + ks * 16 + hl * 8]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, acc, 0, 0, 0);
+            }
+            const int dcol = db * 32 + l32;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int qi = q0 + qb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-                    if (qi < p.Nq)
-                        unsafeAtomicAdd(dQ + (int64_t)qi * p.dq.sn + dcol, acc[e] * p.scale);
-                }
+            for (int e = 0; e < 16; ++e) {
+                const int qi = q0 + qb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                if (qi < p.Nq)
+                    unsafeAtomicAdd(dQ + (int64_t)qi * p.dq.sn + dcol, acc[e] * p.scale);
             }
         }
     }
