@@ -8,22 +8,23 @@
 // reduce-scatter).  With P = exp(sigma*S - LSE) and D_i = dO_i . O_i:
 //   dV = P^T dO,  dS = P o (dO V^T - D),  dK = sigma dS^T Q,  dQ += sigma dS K.
 //
-// Work decomposition
+// Work decomposition (three launches)
 //   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row);
-//   * bwd_main: one workgroup = 4 waves = 128 keys of one (batch, KV head);
-//     each wave keeps its 32 keys' K and V rows in VGPRs and its dK^T, dV^T
-//     accumulators (fp32) for the whole kernel, and loops over the query
+//   * bwd_main (dK, dV): one workgroup = 4 waves = 128 keys of one (batch, KV
+//     head); each wave keeps its 32 keys' K and V rows in VGPRs and its dK^T,
+//     dV^T accumulators (fp32) for the whole kernel, and loops over the query
 //     heads sharing the KV head and over the visible 64-row query tiles; the
 //     next tile's Q, dO rows, LSE and D are loaded into VGPRs (range-checked
-//     buffer loads) while the current tile is computed.
-//     Per tile the scores are recomputed as S = Q K^T with keys in lane
-//     columns (v_mfma_f32_32x32x16_bf16), so P and dS are directly the B
-//     operands of dV^T += dO^T P and dK^T += Q^T dS; the Q^T and dO^T A
-//     operands are read from the row-major Q / dO tiles in LDS with
-//     transposing reads (ds_read_b64_tr_b16).  dS^T goes to LDS (8-byte rows
-//     per lane) and is read back transposed as the A operand of dQ = dS K
-//     (K^T staged in LDS once per workgroup); dQ is added to the fp32 output
-//     with hardware float atomics.
+//     buffer loads) while the current tile is computed.  Per tile the scores
+//     are recomputed as S = Q K^T with keys in lane columns
+//     (v_mfma_f32_32x32x16_bf16), so P and dS are directly the B operands of
+//     dV^T += dO^T P and dK^T += Q^T dS; the Q^T and dO^T A operands are read
+//     from the row-major Q / dO tiles in LDS with transposing reads
+//     (ds_read_b64_tr_b16);
+//   * bwd_dq (dQ): query-tile major, shaped like the forward kernel (below).
+//     Recomputing S and dP there costs two more contractions than sharing
+//     them with bwd_main, but dQ then needs no atomics and no round trip of
+//     dS through LDS, and the result is deterministic.
 #include "common.h"
 
 namespace seqattn {
@@ -91,8 +92,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
 template <int D>
 struct BCfg {
     static constexpr int QSTR = D + 8;         // Q / dO row pitch (bf16)
-    static constexpr int KTSTR = kBKV + 8;     // K^T row pitch
-    static constexpr int DSTR = kBQ + 4;       // dS^T row pitch (rows 8-byte aligned)
     static constexpr int CPT = kBQ * D / 8 / kThreads;  // 16-byte chunks per thread per tile
     static_assert(CPT * kThreads * 8 == kBQ * D, "tile split");
 };
@@ -132,8 +131,6 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     using C = BCfg<D>;
     __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * C::QSTR];
     __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * C::QSTR];
-    __shared__ __attribute__((aligned(16))) bf16 KTs[D * C::KTSTR];
-    __shared__ __attribute__((aligned(16))) bf16 dSTs[kBKV * C::DSTR];
     __shared__ float lse2s[kBQ];
     __shared__ float Dsh[kBQ];
 
@@ -152,32 +149,6 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 
     const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + g * p.k.sh;
     const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + g * p.v.sh;
-
-    // K^T tile of the workgroup in LDS (natural key order), for dQ = dS K
-    for (int blk = tid; blk < (kBKV / 4) * (D / 8); blk += kThreads) {
-        const int kg = blk % (kBKV / 4), dc = blk / (kBKV / 4);
-        unsigned a[4][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = k0 + kg * 4 + u;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (j < p.Nk)
-                x = *(const u32x4 *)(K + (int64_t)j * p.k.sn + dc * 8);
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                a[u][m] = x[m];
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint2 lo, hi;
-            lo.x = (a[0][m] & 0xffffu) | (a[1][m] << 16);
-            lo.y = (a[2][m] & 0xffffu) | (a[3][m] << 16);
-            hi.x = (a[0][m] >> 16) | (a[1][m] & 0xffff0000u);
-            hi.y = (a[2][m] >> 16) | (a[3][m] & 0xffff0000u);
-            *(uint2 *)(&KTs[(dc * 8 + 2 * m) * C::KTSTR + kg * 4]) = lo;
-            *(uint2 *)(&KTs[(dc * 8 + 2 * m + 1) * C::KTSTR + kg * 4]) = hi;
-        }
-    }
 
     // this wave's K and V rows as B operands (k = d): lane holds key `key`,
     // d = 16kk + 8hl .. +8
@@ -247,20 +218,17 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         }
     };
 
-    // transposing-read offsets (see read_tr): P/dS B-operand order for the
-    // Q^T / dO^T operands, natural key order for the dS operand of dQ
+    // transposing-read offset (see read_tr) of the Q^T / dO^T operands, in the
+    // query order of the P / dS accumulator rows
     const int tq_off = (4 * (gg >> 1) + (ip >> 2)) * C::QSTR + 16 * (gg & 1) + 4 * (ip & 3);
-    const int ts_off = (8 * (gg >> 1) + (ip >> 2)) * C::DSTR + 16 * (gg & 1) + 4 * (ip & 3);
 
     if (niters > 0)
         prefetch(0);
 
     for (int it = 0; it < niters; ++it) {
-        const int h = g * group + it / per_head;
         const int q0 = (qt_begin + it % per_head) * kBQ;
-        float *dQ = (float *)p.dq.ptr + b * p.dq.sb + h * p.dq.sh;
 
-        __syncthreads();  // previous iteration done with Qs, dOs, dSTs
+        __syncthreads();  // previous iteration done with Qs, dOs
 #pragma unroll
         for (int u = 0; u < C::CPT; ++u) {
             *(u32x4 *)(&Qs[srow[u] * C::QSTR + scol[u]]) = qreg[u];
@@ -317,9 +285,6 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                 pP[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
                 pS[qb][gq * 2 + 0] = pack_bf16(sv[0], sv[1]);
                 pS[qb][gq * 2 + 1] = pack_bf16(sv[2], sv[3]);
-                // dS^T row `key`, 4 consecutive queries (8 bytes)
-                uint2 w = {pS[qb][gq * 2 + 0], pS[qb][gq * 2 + 1]};
-                *(uint2 *)(&dSTs[(wave * 32 + l32) * C::DSTR + r0]) = w;
             }
         }
 
@@ -340,31 +305,6 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                 const bf16x8 aq = cat_tr(read_tr(&Qs[off]), read_tr(&Qs[off + 8 * C::QSTR]));
                 dVacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bp, dVacc[i], 0, 0, 0);
                 dKacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bs, dKacc[i], 0, 0, 0);
-            }
-        }
-        __syncthreads();  // dS^T of all 128 keys is in LDS
-
-        // ---- dQ[q][d] += sigma * sum_key dS[q][key] K[key][d] ----
-        constexpr int nblk = (kBQ / 32) * (D / 32);
-        for (int ob = wave; ob < nblk; ob += kWaves) {
-            const int qb = ob % (kBQ / 32), db = ob / (kBQ / 32);
-            f32x16 acc;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[e] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < kBKV / 16; ++ks) {
-                const int off = (16 * ks) * C::DSTR + 32 * qb + ts_off;
-                const bf16x8 a = cat_tr(read_tr(&dSTs[off]), read_tr(&dSTs[off + 4 * C::DSTR]));
-                const bf16x8 bk = *(const bf16x8 *)(&KTs[(db * 32 + l32) * C::KTSTR + ks * 16 + hl * 8]);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, acc, 0, 0, 0);
-            }
-            const int dcol = db * 32 + l32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int qi = q0 + qb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-                if (qi < p.Nq)
-                    unsafeAtomicAdd(dQ + (int64_t)qi * p.dq.sn + dcol, acc[e] * p.scale);
             }
         }
     }
@@ -400,6 +340,193 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         }
 }
 
+// ---------------------------------------------------------------------------
+// dQ, query-tile major: one workgroup = 8 waves = 256 query rows of one
+// (batch, query head); wave = 32 rows, whose Q and dO rows are the B operands
+// (VGPRs) of S^T = K Q^T and dP^T = V dO^T.  With queries in lane columns, a
+// lane holds one row's LSE and D, and dS^T = P^T o (dP^T - D) is directly the
+// B operand of dQ^T += K^T dS^T, whose A operand is read from the row-major K
+// tile in LDS with transposing reads.  Each (query, d) is owned by one lane,
+// so dQ is accumulated without atomics (dq += sigma * dQ at the end).
+// ---------------------------------------------------------------------------
+constexpr int kQWaves = 8;
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kQBQ = 32 * kQWaves;
+
+template <int D>
+struct QCfg {
+    static constexpr int BK = 64;               // keys per tile
+    static constexpr int STR = D + 8;           // K / V row pitch (bf16)
+    static constexpr int CPT = BK * D / 8 / kQThreads;  // 16-byte chunks per thread per tile
+    static_assert(CPT * kQThreads * 8 == BK * D, "tile split");
+};
+
+template <int D>
+__global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
+{
+    using C = QCfg<D>;
+    constexpr int BK = C::BK;
+    __shared__ __attribute__((aligned(16))) bf16 Ks[BK * C::STR];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[BK * C::STR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int gg = lane >> 4, ip = lane & 15;
+
+    const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
+    const int BH = p.B * p.Hq;
+    const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // longest first
+    const int bh = (int)(blockIdx.x % BH);
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int g = (int)(((int64_t)h * p.Hkv) / p.Hq);
+
+    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + h * p.q.sh;
+    const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh;
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + g * p.k.sh;
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + g * p.v.sh;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(p.Nq - 1) * p.dout.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, ((int64_t)(p.Nk - 1) * p.k.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, ((int64_t)(p.Nk - 1) * p.v.sn + D) * 2);
+
+    const int q0 = qt * kQBQ;
+    const int q0w = q0 + wave * 32;
+    const int qrow = q0w + l32;
+
+    int kv_end = p.Nk;
+    if (!p.noncausal)
+        kv_end = min(kv_end, max(q0 + kQBQ + p.delta, 0));
+    const int ntiles = (kv_end + BK - 1) / BK;
+    if (ntiles == 0)
+        return;  // no visible key: dq unchanged
+
+    bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        qf[kk] = __builtin_bit_cast(bf16x8, load16(qr, (qrow * (int)p.q.sn + kk * 16 + hl * 8) * 2));
+        of[kk] = __builtin_bit_cast(bf16x8, load16(orr, (qrow * (int)p.dout.sn + kk * 16 + hl * 8) * 2));
+    }
+    float lse2 = INFINITY, dq_d = 0.f;  // +inf: the row contributes P = 0
+    if (qrow < p.Nq) {
+        const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh +
+                           (int64_t)qrow * p.lse.sn);
+        if (lv != -INFINITY)
+            lse2 = lv * kLog2e;
+        dq_d = p.dvec[((int64_t)b * p.Hq + h) * p.Nq + qrow];
+    }
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[i][e] = 0.f;
+    const float c = p.scale * kLog2e;
+
+    u32x4 kreg[C::CPT], vreg[C::CPT];
+    int srow[C::CPT], scol[C::CPT];
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+        const int ch = tid + u * kQThreads;
+        srow[u] = ch / (D / 8);
+        scol[u] = (ch % (D / 8)) * 8;
+    }
+    auto load_tile = [&](int t) {
+        const int j0 = t * BK;
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            kreg[u] = load16(kr, ((j0 + srow[u]) * (int)p.k.sn + scol[u]) * 2);
+            vreg[u] = load16(vr, ((j0 + srow[u]) * (int)p.v.sn + scol[u]) * 2);
+        }
+    };
+    // transposing-read offset of the K^T operand, in the key order of the
+    // dS^T accumulator rows
+    const int tk_off = (4 * (gg >> 1) + (ip >> 2)) * C::STR + 16 * (gg & 1) + 4 * (ip & 3);
+
+    load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            *(u32x4 *)(&Ks[srow[u] * C::STR + scol[u]]) = kreg[u];
+            *(u32x4 *)(&Vs[srow[u] * C::STR + scol[u]]) = vreg[u];
+        }
+        __syncthreads();
+        if (t + 1 < ntiles)
+            load_tile(t + 1);
+
+        const int j0 = t * BK;
+        if (!p.noncausal && j0 > q0w + 31 + p.delta)
+            continue;  // tile entirely in this wave's causal future
+
+        f32x16 s[BK / 32], dp[BK / 32];
+#pragma unroll
+        for (int kb = 0; kb < BK / 32; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                s[kb][e] = dp[kb][e] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const int off = (kb * 32 + l32) * C::STR + kk * 16 + hl * 8;
+                const bf16x8 ak = *(const bf16x8 *)(&Ks[off]);
+                const bf16x8 av = *(const bf16x8 *)(&Vs[off]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], s[kb], 0, 0, 0);
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
+            }
+        }
+        const bool need_mask = (j0 + BK > p.Nk) ||
+                               (!p.noncausal && j0 + BK - 1 > q0w + p.delta);
+        unsigned pS[BK / 32][8];
+#pragma unroll
+        for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                float ds[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + u], c, -lse2));
+                    if (need_mask) {
+                        const int key = j0 + kb * 32 + ((e + u) >> 2) * 8 + hl * 4 + ((e + u) & 3);
+                        const bool vis = key < p.Nk && (p.noncausal || key - qrow <= p.delta);
+                        pe = vis ? pe : 0.f;
+                    }
+                    ds[u] = pe * (dp[kb][e + u] - dq_d);
+                }
+                pS[kb][e >> 1] = pack_bf16(ds[0], ds[1]);
+            }
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int kb = ks >> 1, half = ks & 1;
+            u32x4 w = {pS[kb][half * 4 + 0], pS[kb][half * 4 + 1], pS[kb][half * 4 + 2],
+                       pS[kb][half * 4 + 3]};
+            const bf16x8 bs = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const int off = (16 * ks) * C::STR + 32 * i + tk_off;
+                const bf16x8 a = cat_tr(read_tr(&Ks[off]), read_tr(&Ks[off + 8 * C::STR]));
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[i], 0, 0, 0);
+            }
+        }
+    }
+
+    if (qrow >= p.Nq)
+        return;
+    float *dQ = (float *)p.dq.ptr + b * p.dq.sb + h * p.dq.sh + (int64_t)qrow * p.dq.sn;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = i * 32 + gq * 8 + hl * 4;
+            float4 x = *(float4 *)(dQ + d0);
+            x.x += p.scale * acc[i][gq * 4 + 0];
+            x.y += p.scale * acc[i][gq * 4 + 1];
+            x.z += p.scale * acc[i][gq * 4 + 2];
+            x.w += p.scale * acc[i][gq * 4 + 3];
+            *(float4 *)(dQ + d0) = x;
+        }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st)
@@ -420,6 +547,16 @@ hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st)
         hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     else
         hipLaunchKernelGGL(bwd_main_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t qgrid = (int64_t)((p.Nq + kQBQ - 1) / kQBQ) * p.B * p.Hq;
+    if (qgrid == 0 || p.Nk == 0)
+        return hipSuccess;
+    if (p.d == 128)
+        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
     return hipGetLastError();
 }
 
