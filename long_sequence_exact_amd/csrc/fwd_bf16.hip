@@ -13,9 +13,11 @@
 //   * one workgroup = 8 waves = 256 query rows of one (batch, segment, head);
 //     each wave owns 32 query rows for the whole kernel; two waves share a
 //     SIMD, so one wave's softmax VALU work overlaps the other's MFMAs;
-//   * the workgroup walks the KV segment in tiles of BK keys (64 for d=128,
-//     128 for d=64), staged HBM -> VGPR -> LDS; the next tile's global loads
-//     are issued before the current tile is computed;
+//   * the workgroup walks the KV segment in tiles of 128 keys, staged
+//     HBM -> VGPR -> LDS with range-checked buffer loads (rows past the
+//     segment end read as zeros); the next tile's loads are issued before the
+//     current tile is computed; V stays row-major and is read transposed
+//     (ds_read_b64_tr_b16) as the A operand of the PV product;
 //   * per tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //     (K from LDS as the A operand, Q held in VGPRs as the B operand), so the
 //     accumulator puts one query row in one lane column: the row max needs a
@@ -26,8 +28,8 @@
 //     which fp32 and bf16 hold with full relative precision, and the O
 //     rescale is skipped for most tiles;
 //   * P^T is rounded to bf16 in registers and is directly the B operand of
-//     O^T += V^T P^T; V is transposed while it is written to LDS, in a key
-//     order that matches the accumulator's row interleave;
+//     O^T += V^T P^T; the transposing reads of V deliver keys in the order of
+//     the accumulator's row interleave;
 //   * causal tiles above the diagonal are never visited; only tiles that
 //     straddle it (or the segment tail) are masked;
 //   * workgroups are issued longest-first (last query tile first) with the
@@ -54,7 +56,7 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 
 
 template <int D>
 struct Cfg {
-    static constexpr int BK = (D == 128) ? 64 : 128;  // keys per tile
+    static constexpr int BK = 128;                    // keys per tile
     // LDS row pitches (bf16 elements).  K: +8 so the 32 rows an MFMA operand
     // read touches fall in distinct banks.  V: a pitch of 16 (mod 64) dwords,
     // so the four rows x 32 bytes each 16-lane group of a transposing read
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     __shared__ __attribute__((aligned(16))) bf16 Vs[BK * C::VSTR];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int l32 = lane & 31, hl = lane >> 5;
 
     const int nqt = (p.Nq + kBQ - 1) / kBQ;
@@ -224,6 +227,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[kb], 0, 0, 0);
             }
         }
+        // keep four K operand reads in flight ahead of the MFMA that uses them
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+#pragma unroll
+        for (int i = 0; i < (BK / 32) * (D / 16) - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
         // accumulator element e of block kb: key j0 + 32kb + 8(e/4) + 4hl + e%4,
         // query qrow
