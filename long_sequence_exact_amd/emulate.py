@@ -58,20 +58,50 @@ def sweep_fwd(q, k, v, n_blocks: int, q_block: int, causal: bool, out, lse, scal
     return launches
 
 
-def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None):
+def _blocks(t, P, blk, first_block, count):
+    """View of `count` consecutive length-blk row blocks of t ([1,H,N,d] or
+    [1,H,N]) starting at block `first_block`, as a batch: [count, H, blk(, d)]."""
+    st = t.stride()
+    if t.dim() == 4:
+        return t.as_strided((count, t.shape[1], blk, t.shape[3]),
+                            (blk * st[2], st[1], st[2], st[3]),
+                            t.storage_offset() + first_block * blk * st[2])
+    return t.as_strided((count, t.shape[1], blk), (blk * st[2], st[1], st[2]),
+                        t.storage_offset() + first_block * blk * st[2])
+
+
+def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True):
     """All P ranks of a ring, run one after another on one GPU.
 
     q, k, v: [B,H,N,d]; rank r owns rows [r*N/P, (r+1)*N/P).  Returns the
     merged fp32 output [B,H,N,d] and LSE [B,H,N] of the whole sequence.
+
+    batched=True issues one launch per ring step: at step t the ranks
+    r = t..P-1 hold KV block j = r - t, all with the same offset t*N/P, so
+    they form one strided batch (ranks r < t hold j = r - t + P, which is in
+    the causal future and skipped, or one more batch when non-causal).
+    batched=False issues one launch per (rank, step).
     """
-    n = q.shape[-2]
+    B, H, n, d = q.shape
     blk = n // P
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    for r in range(P):
-        rows = slice(r * blk, (r + 1) * blk)
-        sweep_fwd(q[..., rows, :], k, v, P, r, causal, out[..., rows, :], lse[..., rows],
-                  scale=scale)
+    if not batched or B != 1 or n % P:
+        for r in range(P):
+            rows = slice(r * blk, (r + 1) * blk)
+            sweep_fwd(q[..., rows, :], k, v, P, r, causal, out[..., rows, :], lse[..., rows],
+                      scale=scale)
+        return out, lse
+    for t in range(P):
+        groups = [(t, P - t, 0)]                 # (first rank, ranks, first KV block)
+        if not causal and t > 0:
+            groups.append((0, t, P - t))
+        for r0, cnt, j0 in groups:
+            delta = (r0 - j0) * blk if causal else None
+            attn_segment_fwd(_blocks(q, P, blk, r0, cnt), _blocks(k, P, blk, j0, cnt),
+                             _blocks(v, P, blk, j0, cnt), causal_offset=delta, scale=scale,
+                             out=_blocks(out, P, blk, r0, cnt), lse=_blocks(lse, P, blk, r0, cnt),
+                             accumulate=t > 0)
     return out, lse
 
 

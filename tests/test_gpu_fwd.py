@@ -234,3 +234,18 @@ def test_usp_forward_full_size_sampled():
     lg = to_np(lse).reshape(-1)[rows]
     assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // w.nq,
                   what="usp fwd")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_batched_ring_steps_equal_per_rank_launches(causal):
+    """One launch per ring step (ranks batched through strided views) gives
+    bit-identical results to one launch per (rank, step)."""
+    P, blk, H, d = 8, 200, 2, 128
+    q, k, v = (t.to(DEV) for t in draw([(1, H, P * blk, d)] * 3, 43))
+    a, la = emulate.ring_fwd(q, k, v, P, causal=causal, batched=True)
+    b, lb = emulate.ring_fwd(q, k, v, P, causal=causal, batched=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    if not causal:
+        o_ref, l_ref = oracle.attn_fwd(*(t.float().cpu().numpy() for t in (q, k, v)))
+        assert_parity(to_np(a), to_np(la), o_ref, l_ref, torch.bfloat16, what="ring noncausal")
