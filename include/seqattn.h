@@ -127,8 +127,9 @@ int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
  * segment; ring attention's per-device slices) requires combining partials
  * by their softmax normalisers; no page prints the formula.
  *
- * o_acc: [B, H, N, d] fp32 (in/out); lse_acc: [B, H, N, 1] fp32 (in/out);
- * o_b: same shape, fp32 or bf16; lse_b: fp32.  b must not overlap acc.
+ * o_acc: [B, H, N, d] fp32 (in/out), d a positive multiple of 8;
+ * lse_acc: [B, H, N, 1] fp32 (in/out); o_b: same shape, fp32 or bf16;
+ * lse_b: fp32.  b must not overlap acc.
  * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, HIP.
  */
 int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,

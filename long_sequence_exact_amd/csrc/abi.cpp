@@ -281,8 +281,8 @@ int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
         return st;
     if (o_acc->dtype != SEQATTN_F32)
         return fail(SEQATTN_ERR_DTYPE, "o_acc must be fp32");
-    if (o_acc->d % 4 != 0 || o_acc->d == 0)
-        return fail(SEQATTN_ERR_SHAPE, "d must be a positive multiple of 4");
+    if (o_acc->d % 8 != 0 || o_acc->d == 0)
+        return fail(SEQATTN_ERR_SHAPE, "d must be a positive multiple of 8");
     if (o_b->b != o_acc->b || o_b->h != o_acc->h || o_b->n != o_acc->n || o_b->d != o_acc->d)
         return fail(SEQATTN_ERR_SHAPE, "o_b shape differs from o_acc");
     const seqattn_tensor *ls[2] = {lse_acc, lse_b};

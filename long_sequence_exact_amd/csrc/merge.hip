@@ -7,7 +7,8 @@
 //   O = (wa Oa + wb Ob) / (wa + wb),  L = M + ln(wa + wb),
 // with (0, -inf) as the empty partial.  The merge is bound by HBM bandwidth:
 // each thread moves 16-byte vectors of one row, a row's threads sit in one
-// wavefront so the row's LSE is read once per lane and written by the first.
+// wavefront so the row's LSE is read by each of its lanes (one request) and
+// written by the first.
 #include "common.h"
 
 namespace seqattn {
@@ -15,50 +16,67 @@ namespace {
 
 typedef __bf16 bf16;
 
+// Each thread merges 8 consecutive elements of one row (two 16-byte vectors
+// of the fp32 accumulator, 32 or 16 bytes of the partial), so a wave keeps
+// enough bytes in flight to cover HBM latency; a row's d/8 threads are
+// consecutive lanes of one wave.
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p)
 {
-    const int tpr = p.d / 4;  // threads per row (float4 each)
+    const int tpr = p.d / 8;  // threads per row
     const int64_t total = (int64_t)p.B * p.H * p.N * tpr;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total;
          gid += stride) {
         const int64_t row = gid / tpr;
-        const int c4 = (int)(gid % tpr) * 4;
+        const int c8 = (int)(gid % tpr) * 8;
         const int n = (int)(row % p.N);
         const int64_t bh = row / p.N;
         const int h = (int)(bh % p.H), b = (int)(bh / p.H);
         float *La = (float *)p.la.ptr + b * p.la.sb + h * p.la.sh + (int64_t)n * p.la.sn;
         const float lb = *((const float *)p.lb.ptr + b * p.lb.sb + h * p.lb.sh + (int64_t)n * p.lb.sn);
-        float *Oa = (float *)p.oa.ptr + b * p.oa.sb + h * p.oa.sh + (int64_t)n * p.oa.sn + c4;
-        const int64_t ob_off = b * p.ob.sb + h * p.ob.sh + (int64_t)n * p.ob.sn + c4;
+        float *Oa = (float *)p.oa.ptr + b * p.oa.sb + h * p.oa.sh + (int64_t)n * p.oa.sn + c8;
+        const int64_t ob_off = b * p.ob.sb + h * p.ob.sh + (int64_t)n * p.ob.sn + c8;
         const float la = *La;
-        const float M = fmaxf(la, lb);
-        if (M == -INFINITY) {
-            float4 z = {0.f, 0.f, 0.f, 0.f};
-            *(float4 *)Oa = z;
-            continue;  // LSE stays -inf
-        }
-        const float wa = __expf(la - M), wb = __expf(lb - M);
-        const float tot = wa + wb;
-        const float fa = wa / tot, fb = wb / tot;
-        float4 xb;
+        float4 xa0 = *(const float4 *)Oa, xa1 = *(const float4 *)(Oa + 4);
+        float4 xb0, xb1;
         if (p.ob_f32) {
-            xb = *(const float4 *)((const float *)p.ob.ptr + ob_off);
+            xb0 = *(const float4 *)((const float *)p.ob.ptr + ob_off);
+            xb1 = *(const float4 *)((const float *)p.ob.ptr + ob_off + 4);
         } else {
-            const uint2 raw = *(const uint2 *)((const bf16 *)p.ob.ptr + ob_off);
-            xb.x = __uint_as_float(raw.x << 16);
-            xb.y = __uint_as_float(raw.x & 0xffff0000u);
-            xb.z = __uint_as_float(raw.y << 16);
-            xb.w = __uint_as_float(raw.y & 0xffff0000u);
+            const uint4 raw = *(const uint4 *)((const bf16 *)p.ob.ptr + ob_off);
+            xb0.x = __uint_as_float(raw.x << 16);
+            xb0.y = __uint_as_float(raw.x & 0xffff0000u);
+            xb0.z = __uint_as_float(raw.y << 16);
+            xb0.w = __uint_as_float(raw.y & 0xffff0000u);
+            xb1.x = __uint_as_float(raw.z << 16);
+            xb1.y = __uint_as_float(raw.z & 0xffff0000u);
+            xb1.z = __uint_as_float(raw.w << 16);
+            xb1.w = __uint_as_float(raw.w & 0xffff0000u);
         }
-        float4 xa = *(float4 *)Oa;
-        xa.x = fa * xa.x + fb * xb.x;
-        xa.y = fa * xa.y + fb * xb.y;
-        xa.z = fa * xa.z + fb * xb.z;
-        xa.w = fa * xa.w + fb * xb.w;
-        *(float4 *)Oa = xa;
-        if (c4 == 0)
-            *La = M + __logf(tot);
+        const float M = fmaxf(la, lb);
+        float fa = 0.f, fb = 0.f, lnew = -INFINITY;
+        if (M != -INFINITY) {  // else both partials are empty: (0, -inf)
+            const float wa = __expf(la - M), wb = __expf(lb - M);
+            const float tot = wa + wb;
+            fa = wa / tot;
+            fb = wb / tot;
+            lnew = M + __logf(tot);
+        }
+        if (M == -INFINITY) {  // O of an empty result is 0 whatever the inputs held
+            xa0 = xa1 = xb0 = xb1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        xa0.x = fa * xa0.x + fb * xb0.x;
+        xa0.y = fa * xa0.y + fb * xb0.y;
+        xa0.z = fa * xa0.z + fb * xb0.z;
+        xa0.w = fa * xa0.w + fb * xb0.w;
+        xa1.x = fa * xa1.x + fb * xb1.x;
+        xa1.y = fa * xa1.y + fb * xb1.y;
+        xa1.z = fa * xa1.z + fb * xb1.z;
+        xa1.w = fa * xa1.w + fb * xb1.w;
+        *(float4 *)Oa = xa0;
+        *(float4 *)(Oa + 4) = xa1;
+        if (c8 == 0)
+            *La = lnew;
     }
 }
 
@@ -132,7 +150,7 @@ unsigned grid_for(int64_t threads)
 
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t st)
 {
-    const int64_t threads = (int64_t)p.B * p.H * p.N * (p.d / 4);
+    const int64_t threads = (int64_t)p.B * p.H * p.N * (p.d / 8);
     if (threads == 0)
         return hipSuccess;
     hipLaunchKernelGGL(lse_merge_kernel, dim3(grid_for(threads)), dim3(256), 0, st, p);
