@@ -135,3 +135,37 @@ def test_usp_full_size_sampled_and_invariants():
         sdk = dk[0, g].double().sum(0).cpu()
         mag = dk[0, g].double().abs().sum(0).cpu().max()
         assert sdk.abs().max() <= 1e-3 * mag
+
+
+def test_bwd_sequence_major_layout_views():
+    """Backward on [B, N, H, d]-stored tensors passed as permuted views."""
+    B, N, H, Hkv, d, delta = 1, 300, 4, 2, 128, 0
+    qs, ks, vs, dos = draw([(B, N, H, d), (B, N, Hkv, d), (B, N, Hkv, d), (B, N, H, d)], 2400)
+    q, k, v, do = (t.permute(0, 2, 1, 3) for t in (qs, ks, vs, dos))
+    ref = oracle.attn_bwd(*(t.contiguous().float().numpy() for t in (q, k, v, do)), delta=delta)
+    qd, kd, vd, dod = (t.to(DEV).permute(0, 2, 1, 3) for t in (qs, ks, vs, dos))
+    o, lse = sa.attn_segment_fwd(qd, kd, vd, causal_offset=delta, out_dtype=torch.float32)
+    dq = torch.zeros((B, N, H, d), dtype=torch.float32, device=DEV).permute(0, 2, 1, 3)
+    dk = torch.empty((B, N, Hkv, d), dtype=torch.float32, device=DEV).permute(0, 2, 1, 3)
+    dv = torch.empty((B, N, Hkv, d), dtype=torch.float32, device=DEV).permute(0, 2, 1, 3)
+    sa.attn_segment_bwd(qd, kd, vd, o, lse, dod, causal_offset=delta, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    _grads_parity(dq, dk, dv, ref, "bwd seq-major")
+
+
+def test_bwd_empty_and_fully_masked_segments():
+    """A KV segment entirely in the queries' causal future contributes nothing:
+    dq unchanged, dk = dv = 0; an empty query block gives dk = dv = 0."""
+    q, k, v, do = (t.to(DEV) for t in draw([(1, 2, 128, 128), (1, 1, 256, 128),
+                                             (1, 1, 256, 128), (1, 2, 128, 128)], 2500))
+    o, lse = sa.attn_segment_fwd(q, k, v, causal_offset=0, out_dtype=torch.float32)
+    dq0 = torch.randn(q.shape, device=DEV)
+    dq = dq0.clone()
+    _, dk, dv = sa.attn_segment_bwd(q, k, v, o, lse, do, causal_offset=-1000, dq=dq)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq0)
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+    qz = q[..., :0, :]
+    _, dk2, dv2 = sa.attn_segment_bwd(qz, k, v, o[..., :0, :], lse[..., :0], do[..., :0, :])
+    torch.cuda.synchronize()
+    assert torch.all(dk2 == 0) and torch.all(dv2 == 0)

@@ -249,3 +249,19 @@ def test_batched_ring_steps_equal_per_rank_launches(causal):
     if not causal:
         o_ref, l_ref = oracle.attn_fwd(*(t.float().cpu().numpy() for t in (q, k, v)))
         assert_parity(to_np(a), to_np(la), o_ref, l_ref, torch.bfloat16, what="ring noncausal")
+
+
+def test_sequence_major_layout_views():
+    """Q/K/V stored [B, N, H, d] (the sequence-sharded layout before Ulysses'
+    all-to-all) and passed as permuted [B, H, N, d] views (stride_n = H*d)."""
+    B, N, H, Hkv, d = 2, 700, 4, 2, 128
+    qs, ks, vs = draw([(B, N, H, d), (B, N, Hkv, d), (B, N, Hkv, d)], 61)
+    q, k, v = (t.permute(0, 2, 1, 3) for t in (qs, ks, vs))
+    o_ref, l_ref = oracle.attn_fwd(*(t.contiguous().float().numpy() for t in (q, k, v)), delta=0)
+    qd, kd, vd = (t.to(DEV).permute(0, 2, 1, 3) for t in (qs, ks, vs))
+    assert qd.stride(2) == H * d
+    out = torch.empty((B, N, H, d), dtype=torch.float32, device=DEV).permute(0, 2, 1, 3)
+    lse = torch.empty((B, N, H), dtype=torch.float32, device=DEV).permute(0, 2, 1)
+    sa.attn_segment_fwd(qd, kd, vd, causal_offset=0, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert_parity(to_np(out), to_np(lse), o_ref, l_ref, torch.bfloat16, what="seq-major")
