@@ -10,13 +10,14 @@
 //
 // Work decomposition (three launches)
 //   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row);
-//   * bwd_main (dK, dV): one workgroup = 4 waves = 128 keys of one (batch, KV
-//     head); each wave keeps its 32 keys' K and V rows in VGPRs and its dK^T,
-//     dV^T accumulators (fp32) for the whole kernel, and loops over the query
-//     heads sharing the KV head and over the visible 64-row query tiles; the
-//     next tile's Q, dO rows, LSE and D are loaded into VGPRs (range-checked
-//     buffer loads) while the current tile is computed.  Per tile the scores
-//     are recomputed as S = Q K^T with keys in lane columns
+//   * bwd_main (dK, dV): one workgroup = 8 waves for 128 keys of one (batch,
+//     KV head): waves 0-3 accumulate dV^T and waves 4-7 dK^T for the same
+//     4 x 32 keys (one fp32 accumulator per wave keeps two waves per SIMD;
+//     S is computed by both), looping over the query heads sharing the KV
+//     head and over the visible 64-row query tiles; the next tile's Q, dO
+//     rows, LSE and D are loaded into VGPRs (range-checked buffer loads)
+//     while the current tile is computed.  Per tile the scores are
+//     recomputed as S = Q K^T with keys in lane columns
 //     (v_mfma_f32_32x32x16_bf16), so P and dS are directly the B operands of
 //     dV^T += dO^T P and dK^T += Q^T dS; the Q^T and dO^T A operands are read
 //     from the row-major Q / dO tiles in LDS with transposing reads
@@ -35,9 +36,9 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBKV = 32 * kWaves;  // keys per workgroup
+constexpr int kBKV = 128;          // keys per workgroup (32 per wave pair)
 constexpr int kBQ = 64;            // query rows per iteration
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -135,7 +136,11 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     __shared__ float Dsh[kBQ];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // waves 0-3 form dV, waves 4-7 form dK, for the same 4 x 32 keys: every
+    // wave holds one fp32 accumulator and two waves share each SIMD
+    const bool is_dk = wave >= 4;
     const int l32 = lane & 31, hl = lane >> 5;
     const int gg = lane >> 4, ip = lane & 15;
 
@@ -144,32 +149,33 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const int bg = (int)(blockIdx.x / nkt);
     const int g = bg % p.Hkv, b = bg / p.Hkv;
     const int k0 = kt * kBKV;
-    const int kw0 = k0 + wave * 32;
+    const int kw0 = k0 + (wave & 3) * 32;
     const int key = kw0 + l32;  // this lane's key (accumulator column)
 
     const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + g * p.k.sh;
     const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + g * p.v.sh;
 
-    // this wave's K and V rows as B operands (k = d): lane holds key `key`,
-    // d = 16kk + 8hl .. +8
+    // the wave's K rows (and, for dK, V rows) as B operands (k = d): lane
+    // holds key `key`, d = 16kk + 8hl .. +8
     bf16x8 kB[D / 16], vB[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
         if (key < p.Nk) {
             xk = *(const u32x4 *)(K + (int64_t)key * p.k.sn + kk * 16 + hl * 8);
-            xv = *(const u32x4 *)(V + (int64_t)key * p.v.sn + kk * 16 + hl * 8);
+            if (is_dk)
+                xv = *(const u32x4 *)(V + (int64_t)key * p.v.sn + kk * 16 + hl * 8);
         }
         kB[kk] = __builtin_bit_cast(bf16x8, xk);
         vB[kk] = __builtin_bit_cast(bf16x8, xv);
     }
 
-    f32x16 dKacc[D / 32], dVacc[D / 32];
+    f32x16 acc[D / 32];  // dV^T (waves 0-3) or dK^T / sigma (waves 4-7)
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            dKacc[i][e] = dVacc[i][e] = 0.f;
+            acc[i][e] = 0.f;
 
     const float c = p.scale * kLog2e;
     const int group = p.Hq / p.Hkv;
@@ -221,6 +227,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     // transposing-read offset (see read_tr) of the Q^T / dO^T operands, in the
     // query order of the P / dS accumulator rows
     const int tq_off = (4 * (gg >> 1) + (ip >> 2)) * C::QSTR + 16 * (gg & 1) + 4 * (ip & 3);
+    const bf16 *At = is_dk ? Qs : dOs;  // A operand of dK^T += Q^T dS / dV^T += dO^T P
 
     if (niters > 0)
         prefetch(0);
@@ -242,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         if (it + 1 < niters)
             prefetch(it + 1);
 
-        // ---- S = Q K^T, dP = dO V^T for 2 blocks of 32 queries ----
+        // ---- S = Q K^T (and dP = dO V^T for dK) for 2 blocks of 32 queries ----
         const bool need_mask = (k0 + kBKV > p.Nk) || (q0 + kBQ > p.Nq) ||
                                (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
-        unsigned pP[2][8], pS[2][8];
+        unsigned pB[2][8];  // P (dV waves) or dS (dK waves), bf16 pairs
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             f32x16 s, dp;
@@ -255,19 +262,22 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
                 const bf16x8 aq = *(const bf16x8 *)(&Qs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
-                const bf16x8 ad = *(const bf16x8 *)(&dOs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
+            }
+            if (is_dk) {
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const bf16x8 ad = *(const bf16x8 *)(&dOs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
+                }
             }
             // element e: query row qb*32 + 8(e/4) + 4hl + e%4 of the tile
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int r0 = qb * 32 + gq * 8 + hl * 4;
                 const float4 l2 = *(const float4 *)(&lse2s[r0]);
-                const float4 dd = *(const float4 *)(&Dsh[r0]);
                 const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-                const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
-                float pv[4], sv[4];
+                float pv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int e = gq * 4 + u;
@@ -279,63 +289,55 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                         pe = vis ? pe : 0.f;
                     }
                     pv[u] = pe;
-                    sv[u] = pe * (dp[e] - dv[u]);
                 }
-                pP[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
-                pP[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
-                pS[qb][gq * 2 + 0] = pack_bf16(sv[0], sv[1]);
-                pS[qb][gq * 2 + 1] = pack_bf16(sv[2], sv[3]);
+                if (is_dk) {
+                    const float4 dd = *(const float4 *)(&Dsh[r0]);
+                    pv[0] *= dp[gq * 4 + 0] - dd.x;
+                    pv[1] *= dp[gq * 4 + 1] - dd.y;
+                    pv[2] *= dp[gq * 4 + 2] - dd.z;
+                    pv[3] *= dp[gq * 4 + 3] - dd.w;
+                }
+                pB[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
+                pB[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
             }
         }
 
-        // ---- dV^T += dO^T P, dK^T += Q^T dS (k = the tile's 64 query rows) ----
+        // ---- dV^T += dO^T P or dK^T += Q^T dS (k = the tile's 64 query rows) ----
 #pragma unroll
         for (int ks = 0; ks < kBQ / 16; ++ks) {
             const int qb = ks >> 1, half = ks & 1;
-            u32x4 wp = {pP[qb][half * 4 + 0], pP[qb][half * 4 + 1], pP[qb][half * 4 + 2],
-                        pP[qb][half * 4 + 3]};
-            u32x4 ws = {pS[qb][half * 4 + 0], pS[qb][half * 4 + 1], pS[qb][half * 4 + 2],
-                        pS[qb][half * 4 + 3]};
-            const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
-            const bf16x8 bs = __builtin_bit_cast(bf16x8, ws);
+            u32x4 w = {pB[qb][half * 4 + 0], pB[qb][half * 4 + 1], pB[qb][half * 4 + 2],
+                       pB[qb][half * 4 + 3]};
+            const bf16x8 bb = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
                 const int off = (16 * ks) * C::QSTR + 32 * i + tq_off;
-                const bf16x8 ad = cat_tr(read_tr(&dOs[off]), read_tr(&dOs[off + 8 * C::QSTR]));
-                const bf16x8 aq = cat_tr(read_tr(&Qs[off]), read_tr(&Qs[off + 8 * C::QSTR]));
-                dVacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bp, dVacc[i], 0, 0, 0);
-                dKacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bs, dKacc[i], 0, 0, 0);
+                const bf16x8 a = cat_tr(read_tr(&At[off]), read_tr(&At[off + 8 * C::QSTR]));
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[i], 0, 0, 0);
             }
         }
     }
 
-    // ---- write dK = sigma dK^T^T, dV (key rows, 4 consecutive d per store) ----
+    // ---- write dK = sigma (dK^T)^T or dV (key rows, 4 consecutive d per store) ----
     if (key >= p.Nk)
         return;
-    const int64_t krow_k = b * p.dk.sb + g * p.dk.sh + (int64_t)key * p.dk.sn;
-    const int64_t krow_v = b * p.dv.sb + g * p.dv.sh + (int64_t)key * p.dv.sn;
+    const View &out = is_dk ? p.dk : p.dv;
+    const int out_f32 = is_dk ? p.dk_f32 : p.dv_f32;
+    const float f = is_dk ? p.scale : 1.f;
+    const int64_t krow = b * out.sb + g * out.sh + (int64_t)key * out.sn;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int d0 = i * 32 + gq * 8 + hl * 4;
-            const float k0v = dKacc[i][gq * 4 + 0] * p.scale, k1v = dKacc[i][gq * 4 + 1] * p.scale;
-            const float k2v = dKacc[i][gq * 4 + 2] * p.scale, k3v = dKacc[i][gq * 4 + 3] * p.scale;
-            const float v0 = dVacc[i][gq * 4 + 0], v1 = dVacc[i][gq * 4 + 1];
-            const float v2 = dVacc[i][gq * 4 + 2], v3 = dVacc[i][gq * 4 + 3];
-            if (p.dk_f32) {
-                float4 w = {k0v, k1v, k2v, k3v};
-                *(float4 *)((float *)p.dk.ptr + krow_k + d0) = w;
+            const float x0 = acc[i][gq * 4 + 0] * f, x1 = acc[i][gq * 4 + 1] * f;
+            const float x2 = acc[i][gq * 4 + 2] * f, x3 = acc[i][gq * 4 + 3] * f;
+            if (out_f32) {
+                float4 w = {x0, x1, x2, x3};
+                *(float4 *)((float *)out.ptr + krow + d0) = w;
             } else {
-                uint2 w = {pack_bf16(k0v, k1v), pack_bf16(k2v, k3v)};
-                *(uint2 *)((bf16 *)p.dk.ptr + krow_k + d0) = w;
-            }
-            if (p.dv_f32) {
-                float4 w = {v0, v1, v2, v3};
-                *(float4 *)((float *)p.dv.ptr + krow_v + d0) = w;
-            } else {
-                uint2 w = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
-                *(uint2 *)((bf16 *)p.dv.ptr + krow_v + d0) = w;
+                uint2 w = {pack_bf16(x0, x1), pack_bf16(x2, x3)};
+                *(uint2 *)((bf16 *)out.ptr + krow + d0) = w;
             }
         }
 }
