@@ -428,3 +428,142 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Dilated attention backward                                                */
+/* ------------------------------------------------------------------------- */
+
+/* Key list of query p in branch b (segment-relative dilation; causal keeps
+ * keys at original positions <= p).  Returns the count; 0 if p is not
+ * selected by the branch. */
+static int64_t dilated_keys(int64_t p, int64_t N, int64_t w, int64_t r,
+                            int32_t causal, int64_t *keys)
+{
+    if ((p % w) % r != 0)
+        return 0;
+    const int64_t seg0 = (p / w) * w;
+    int64_t n = 0;
+    for (int64_t t = seg0; t < seg0 + w && t < N; t += r)
+        if (!causal || t <= p)
+            keys[n++] = t;
+    return n;
+}
+
+/*
+ * oracle_dilated_bwd: gradients of L = sum(dO * O) for the dilated attention
+ * of oracle_dilated_fwd.  Folding branch partials with the log-sum-exp merge
+ * is one softmax over the list of (branch, key) occurrences of query p, so
+ * with the global O_p, LSE_p and D_p = dO_p . O_p, every occurrence (b, j)
+ * contributes P = exp(s_pj - LSE_p), dS = P (dO_p . v_j - D_p):
+ *   dV_j += P dO_p,  dQ_p += sigma dS k_j,  dK_j += sigma dS q_p.
+ * Full outputs: dq [B][Hq][N][d], dk and dv [B][Hkv][N][d].
+ */
+void oracle_dilated_bwd(const float *q, const float *k, const float *v,
+                        const float *dout, int64_t B, int64_t Hq, int64_t Hkv,
+                        int64_t N, int64_t d, const int64_t *w, const int64_t *r,
+                        int32_t nb, int32_t causal, double scale,
+                        double *dq_out, double *dk_out, double *dv_out)
+{
+    const double sigma = pick_scale(scale, d);
+    const int64_t nq_rows = B * Hq * N;
+    double *o = (double *)malloc(sizeof(double) * (nq_rows > 0 ? nq_rows : 1) * d);
+    double *lse = (double *)malloc(sizeof(double) * (nq_rows > 0 ? nq_rows : 1));
+    double *D = (double *)malloc(sizeof(double) * (nq_rows > 0 ? nq_rows : 1));
+    int64_t wmax = 1;
+    for (int32_t b = 0; b < nb; ++b)
+        if (w[b] > wmax)
+            wmax = w[b];
+
+    /* global O, LSE (the forward definition) and D per query row */
+    oracle_dilated_fwd(q, k, v, B, Hq, Hkv, N, d, w, r, nb, causal, scale, NULL,
+                       nq_rows, o, lse);
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < nq_rows; ++row) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            acc += (double)dout[row * d + c] * o[row * d + c];
+        D[row] = acc;
+    }
+
+    /* dQ per query row */
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * wmax);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t row = 0; row < nq_rows; ++row) {
+            const int64_t p = row % N, bh = row / N;
+            const int64_t bt = bh / Hq, h = bh % Hq;
+            const int64_t g = kv_head_of(h, Hq, Hkv);
+            const float *qrow = q + row * d, *dorow = dout + row * d;
+            double *dq = dq_out + row * d;
+            for (int64_t c = 0; c < d; ++c)
+                dq[c] = 0.0;
+            for (int32_t b = 0; b < nb; ++b) {
+                const int64_t n = dilated_keys(p, N, w[b], r[b], causal, keys);
+                for (int64_t t = 0; t < n; ++t) {
+                    const float *krow = k + ((bt * Hkv + g) * N + keys[t]) * d;
+                    const float *vrow = v + ((bt * Hkv + g) * N + keys[t]) * d;
+                    double dot = 0.0, dp = 0.0;
+                    for (int64_t c = 0; c < d; ++c) {
+                        dot += (double)qrow[c] * (double)krow[c];
+                        dp += (double)dorow[c] * (double)vrow[c];
+                    }
+                    const double P = exp(sigma * dot - lse[row]);
+                    const double ds = P * (dp - D[row]);
+                    for (int64_t c = 0; c < d; ++c)
+                        dq[c] += sigma * ds * (double)krow[c];
+                }
+            }
+        }
+        free(keys);
+    }
+
+    /* dK, dV per key row: every (branch, query) that lists the key */
+    const int64_t nk_rows = B * Hkv * N;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * wmax);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t kr = 0; kr < nk_rows; ++kr) {
+            const int64_t j = kr % N, bg = kr / N;
+            const int64_t bt = bg / Hkv, g = bg % Hkv;
+            const float *krow = k + kr * d, *vrow = v + kr * d;
+            double *dk = dk_out + kr * d, *dv = dv_out + kr * d;
+            for (int64_t c = 0; c < d; ++c)
+                dk[c] = dv[c] = 0.0;
+            for (int64_t h = 0; h < Hq; ++h) {
+                if (kv_head_of(h, Hq, Hkv) != g)
+                    continue;
+                for (int32_t b = 0; b < nb; ++b) {
+                    const int64_t seg0 = (j / w[b]) * w[b];
+                    for (int64_t p = seg0; p < seg0 + w[b] && p < N; ++p) {
+                        const int64_t n = dilated_keys(p, N, w[b], r[b], causal, keys);
+                        int listed = 0;
+                        for (int64_t t = 0; t < n; ++t)
+                            if (keys[t] == j)
+                                listed = 1;
+                        if (!listed)
+                            continue;
+                        const int64_t row = (bt * Hq + h) * N + p;
+                        const float *qrow = q + row * d, *dorow = dout + row * d;
+                        double dot = 0.0, dp = 0.0;
+                        for (int64_t c = 0; c < d; ++c) {
+                            dot += (double)qrow[c] * (double)krow[c];
+                            dp += (double)dorow[c] * (double)vrow[c];
+                        }
+                        const double P = exp(sigma * dot - lse[row]);
+                        const double ds = P * (dp - D[row]);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dv[c] += P * (double)dorow[c];
+                            dk[c] += sigma * ds * (double)qrow[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(keys);
+    }
+    free(o);
+    free(lse);
+    free(D);
+}

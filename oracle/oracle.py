@@ -54,9 +54,11 @@ def _load():
     lib.oracle_attn_bwd_dq_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D,
                                             P, I, P, P, P]
     lib.oracle_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P, P]
+    lib.oracle_dilated_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, P, ctypes.c_int32,
+                                       ctypes.c_int32, D, P, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     for f in ("oracle_attn_fwd", "oracle_lse_merge", "oracle_dilated_fwd",
-              "oracle_attn_bwd_dq_rows", "oracle_attn_bwd"):
+              "oracle_attn_bwd_dq_rows", "oracle_attn_bwd", "oracle_dilated_bwd"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -186,6 +188,25 @@ def attn_bwd(q, k, v, dout, delta=NONCAUSAL, scale=0.0):
     lib.oracle_attn_bwd(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(do4), B, Hq, Hkv, Nq,
                         Nk, d, int(delta), float(scale), _ptr(dq), _ptr(dk),
                         _ptr(dv))
+    if np.asarray(q).ndim == 3:
+        return dq[0], dk[0], dv[0]
+    return dq, dk, dv
+
+
+def dilated_bwd(q, k, v, dout, segment_lengths, dilations, causal=False, scale=0.0):
+    """(dQ, dK, dV) of L = sum(dO * O) for dilated_fwd's attention."""
+    lib = _load()
+    q4, k4, v4, do4 = _as4(q), _as4(k), _as4(v), _as4(dout)
+    B, Hq, N, d = q4.shape
+    Hkv = k4.shape[1]
+    w = np.ascontiguousarray(segment_lengths, np.int64)
+    rr = np.ascontiguousarray(dilations, np.int64)
+    dq = np.empty((B, Hq, N, d), np.float64)
+    dk = np.empty((B, Hkv, N, d), np.float64)
+    dv = np.empty((B, Hkv, N, d), np.float64)
+    lib.oracle_dilated_bwd(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(do4), B, Hq, Hkv, N, d,
+                           _ptr(w), _ptr(rr), len(w), int(bool(causal)), float(scale),
+                           _ptr(dq), _ptr(dk), _ptr(dv))
     if np.asarray(q).ndim == 3:
         return dq[0], dk[0], dv[0]
     return dq, dk, dv

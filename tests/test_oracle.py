@@ -434,3 +434,78 @@ def test_dilated_row_subset():
     o2, l2 = oracle.dilated_fwd(q, k, v, (16, 32, 64), (1, 2, 4), rows=rows)
     assert np.array_equal(o2, o.reshape(-1, d)[rows])
     assert np.array_equal(l2, l.reshape(-1)[rows])
+
+
+# --------------------------------------------------------------------------
+# dilated attention backward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ws,rs,causal,group", [
+    ((8, 16, 32), (1, 2, 4), False, 1),
+    ((8, 16, 32), (1, 2, 4), True, 2),
+    ((12, 24), (2, 6), False, 1),          # unselected positions, r not 2^k
+])
+def test_dilated_bwd_matches_library_autograd(ws, rs, causal, group):
+    # Library autograd through attention with the additive log-multiplicity
+    # bias (the multiset-union form of the branch fold).
+    n, d = 32, 8
+    q = _rand((1, 2 * group, n, d), 400)
+    k = _rand((1, 2, n, d), 401)
+    v = _rand((1, 2, n, d), 402)
+    do = _rand((1, 2 * group, n, d), 403)
+    dq, dk, dv = oracle.dilated_bwd(q, k, v, do, ws, rs, causal=causal)
+    c = _multiplicity(n, ws, rs, causal)
+    live = c.sum(1) > 0
+    with np.errstate(divide="ignore"):
+        bias = torch.from_numpy(np.log(c[live]))
+    qt = torch.from_numpy(q.astype(np.float64)).requires_grad_()
+    kt = torch.from_numpy(k.astype(np.float64)).requires_grad_()
+    vt = torch.from_numpy(v.astype(np.float64)).requires_grad_()
+    o = F.scaled_dot_product_attention(qt[:, :, live], kt.repeat_interleave(group, 1),
+                                       vt.repeat_interleave(group, 1), attn_mask=bias)
+    (o * torch.from_numpy(do[:, :, live].astype(np.float64))).sum().backward()
+    assert np.abs(dq - qt.grad.numpy()).max() < 1e-12
+    assert np.abs(dk - kt.grad.numpy()).max() < 1e-12
+    assert np.abs(dv - vt.grad.numpy()).max() < 1e-12
+    assert np.all(dq[:, :, ~live] == 0)
+
+
+def test_dilated_bwd_finite_differences():
+    n, d = 12, 4
+    ws, rs = (4, 12), (1, 3)
+    q = _rand((1, 1, n, d), 410, quant=6)
+    k = _rand((1, 1, n, d), 411, quant=6)
+    v = _rand((1, 1, n, d), 412, quant=6)
+    do = _rand((1, 1, n, d), 413, quant=6)
+    dq, dk, dv = oracle.dilated_bwd(q, k, v, do, ws, rs)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.dilated_fwd(qq, kk, vv, ws, rs)
+        return float((o * do.astype(np.float64)).sum())
+
+    def fd(which, idx, h):
+        args = [q.copy(), k.copy(), v.copy()]
+        args[which][idx] += np.float32(h)
+        lp = loss(*args)
+        args[which][idx] -= np.float32(2 * h)
+        return (lp - loss(*args)) / (2 * h)
+
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        arr = (q, k, v)[which]
+        for idx in np.ndindex(arr.shape):
+            h = 2.0 ** -9
+            g = (4 * fd(which, idx, h / 2) - fd(which, idx, h)) / 3
+            assert abs(g - grad[idx]) < 1e-8 * max(1.0, abs(grad[idx])), (which, idx)
+
+
+def test_dilated_bwd_invariants():
+    # every position selected by the dense first branch: sum_j dV_j = sum_p dO_p
+    # and sum_j dK_j = 0 per KV head
+    n, d = 64, 8
+    q = _rand((1, 2, n, d), 420)
+    k = _rand((1, 1, n, d), 421)
+    v = _rand((1, 1, n, d), 422)
+    do = _rand((1, 2, n, d), 423)
+    _, dk, dv = oracle.dilated_bwd(q, k, v, do, (16, 32, 64), (1, 2, 4), causal=True)
+    assert np.abs(dv.sum(axis=2)[0, 0] - do.astype(np.float64).sum(axis=(1, 2))[0]).max() < 1e-12
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12

@@ -36,6 +36,10 @@ MUTANTS = {
     "dilated_causal_strict": ("if (!causal || t <= p)", "if (!causal || t < p)"),
     "dilated_merge_drops_branch": ("merge_row(acc, lacc, ob, lb, d, tmp, &lnew);",
                                    "merge_row(ob, lb, ob, lb, d, tmp, &lnew);"),
+    "dilated_bwd_dk_misses_scale": ("dk[c] += sigma * ds * (double)qrow[c];\n                        }\n                    }\n                }\n            }\n        }\n        free(keys);",
+                                    "dk[c] += ds * (double)qrow[c];\n                        }\n                    }\n                }\n            }\n        }\n        free(keys);"),
+    "dilated_bwd_uses_local_lse": ("const double P = exp(sigma * dot - lse[row]);\n                    const double ds = P * (dp - D[row]);\n                    for (int64_t c = 0; c < d; ++c)\n                        dq[c] += sigma * ds * (double)krow[c];\n                }",
+                                   "const double P = exp(sigma * dot - lse[row] + 0.1);\n                    const double ds = P * (dp - D[row]);\n                    for (int64_t c = 0; c < d; ++c)\n                        dq[c] += sigma * ds * (double)krow[c];\n                }"),
 }
 
 
