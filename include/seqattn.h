@@ -86,6 +86,7 @@ typedef struct {
 #define SEQATTN_OP_LSE_MERGE 1
 #define SEQATTN_OP_DILATED_FWD 2
 #define SEQATTN_OP_SEGMENT_BWD 3
+#define SEQATTN_OP_DILATED_BWD 4
 
 /*
  * seqattn_attn_segment_fwd -- partial attention of a query block against one
@@ -184,15 +185,47 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
  * q, d_o: [B, Hq, Nq, d] bf16; k, v: [B, Hkv, Nk, d] bf16; o: [B, Hq, Nq, d]
  * bf16 or fp32; lse: [B, Hq, Nq, 1] fp32.
  * dq: [B, Hq, Nq, d] fp32, ACCUMULATED (dq += ...), so a sweep over
- * segments sums into it; dk, dv: [B, Hkv, Nk, d] fp32 or bf16, OVERWRITTEN.
+ * segments sums into it; dk, dv: [B, Hkv, Nk, d] fp32 or bf16, OVERWRITTEN
+ * (flags 0) or, with SEQATTN_ACCUMULATE, fp32 and ACCUMULATED.
  * workspace: seqattn_workspace_size(SEQATTN_OP_SEGMENT_BWD) bytes.
  * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, WORKSPACE, UNSUPPORTED (fp32
- * inputs), HIP.
+ * inputs, unknown flags), HIP.
  */
 int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              const seqattn_tensor *v, const seqattn_tensor *o,
                              const seqattn_tensor *lse,
                              const seqattn_tensor *d_o, int64_t causal_offset,
+                             float softmax_scale, uint32_t flags,
+                             seqattn_tensor *dq, seqattn_tensor *dk,
+                             seqattn_tensor *dv, void *workspace,
+                             size_t workspace_bytes, void *hip_stream);
+
+/*
+ * seqattn_dilated_attn_bwd -- gradients of seqattn_dilated_attn_fwd.
+ *
+ * Passage: "LongNet: Scaling Transformers to 1,000,000,000 Tokens",
+ * Abstract and Results (dilated attention, the mixture of (w, r) branches)
+ * and Distributed Trainer (training through it; the backward forms the
+ * gradients of exactly the keys/values each query attended to).
+ *
+ * The merged output is one softmax over the union of every branch's keys,
+ * each key counted once per branch that lists it, so with the merged LSE and
+ * D_i = sum_c dO_ic O_ic, each branch's selected (query, key) pairs take the
+ * segment backward above, and the gradients of all branches add up.
+ * q, d_o: [B, Hq, N, d] bf16; k, v: [B, Hkv, N, d] bf16; o: [B, Hq, N, d]
+ * bf16 or fp32 and lse: [B, Hq, N, 1] fp32, both from the forward with the
+ * same (segment_lengths, dilations, flags).  flags: SEQATTN_CAUSAL or 0.
+ * dq: fp32, ACCUMULATED; dk, dv: [B, Hkv, N, d] fp32, OVERWRITTEN (rows no
+ * branch selects get 0).
+ * workspace: seqattn_workspace_size(SEQATTN_OP_DILATED_BWD) bytes.
+ * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, WORKSPACE, UNSUPPORTED, HIP.
+ */
+int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, const seqattn_tensor *o,
+                             const seqattn_tensor *lse,
+                             const seqattn_tensor *d_o,
+                             const int64_t *segment_lengths,
+                             const int64_t *dilations, int32_t n_branches,
                              float softmax_scale, uint32_t flags,
                              seqattn_tensor *dq, seqattn_tensor *dk,
                              seqattn_tensor *dv, void *workspace,

@@ -8,6 +8,7 @@ torch's current stream.  All computation happens in the library's kernels.
     lse_merge(o_acc, lse_acc, o_b, lse_b)               (in place)
     dilated_attn_fwd(q, k, v, segment_lengths, dilations, causal=False) -> (o, lse)
     attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, ...) -> (dq, dk, dv)
+    dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, ...) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ from . import _lib
 from ._lib import ACCUMULATE, CAUSAL, NONCAUSAL, SeqattnError
 
 __all__ = ["attn_segment_fwd", "lse_merge", "dilated_attn_fwd", "attn_segment_bwd",
-           "workspace_size", "NONCAUSAL", "SeqattnError", "version"]
+           "dilated_attn_bwd", "workspace_size", "NONCAUSAL", "SeqattnError", "version"]
 
 
 def version() -> int:
@@ -102,10 +103,12 @@ def dilated_attn_fwd(q, k, v, segment_lengths, dilations, causal=False, scale=No
 
 
 def attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, scale=None, dq=None,
-                     dk=None, dv=None, grad_dtype=torch.float32, workspace=None):
+                     dk=None, dv=None, grad_dtype=torch.float32, workspace=None,
+                     accumulate_kv=False):
     """Gradients of one (query block, KV segment) pair from the global O/LSE.
 
-    dq (fp32) is accumulated into (zeros if not given); dk, dv are written.
+    dq (fp32) is accumulated into (zeros if not given); dk, dv are written,
+    or, with accumulate_kv=True, accumulated (fp32).
     """
     L = _lib.lib()
     if dq is None:
@@ -127,6 +130,43 @@ def attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, scale=None, dq=No
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(L.seqattn_attn_segment_bwd(
         *[ctypes.byref(x) for x in ds], ctypes.byref(dl), ctypes.byref(ddo), delta,
-        float(scale or 0.0), 0, ctypes.byref(gq), ctypes.byref(gk), ctypes.byref(gv),
-        ctypes.c_void_p(wptr), wbytes, ctypes.c_void_p(_lib.stream_handle())))
+        float(scale or 0.0), ACCUMULATE if accumulate_kv else 0, ctypes.byref(gq),
+        ctypes.byref(gk), ctypes.byref(gv), ctypes.c_void_p(wptr), wbytes,
+        ctypes.c_void_p(_lib.stream_handle())))
+    return dq, dk, dv
+
+
+def dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, causal=False,
+                     scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of dilated_attn_fwd from its merged (o, lse).
+
+    dq (fp32) is accumulated into (zeros if not given); dk, dv (fp32) are written.
+    """
+    L = _lib.lib()
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    n = len(segment_lengths)
+    if len(dilations) != n:
+        raise ValueError("segment_lengths and dilations differ in length")
+    w = (ctypes.c_int64 * n)(*[int(x) for x in segment_lengths])
+    r = (ctypes.c_int64 * n)(*[int(x) for x in dilations])
+    ds = [_lib.desc(t) for t in (q, k, v, o)]
+    dl = _lib.desc(lse, lse=True)
+    ddo = _lib.desc(d_o)
+    gq, gk, gv = _lib.desc(dq), _lib.desc(dk), _lib.desc(dv)
+    need = int(L.seqattn_workspace_size(_lib.OP_DILATED_BWD, ctypes.byref(ds[0]),
+                                        ctypes.byref(ds[1]), n))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(L.seqattn_dilated_attn_bwd(
+        *[ctypes.byref(x) for x in ds], ctypes.byref(dl), ctypes.byref(ddo), w, r, n,
+        float(scale or 0.0), CAUSAL if causal else 0, ctypes.byref(gq), ctypes.byref(gk),
+        ctypes.byref(gv), ctypes.c_void_p(wptr), wbytes,
+        ctypes.c_void_p(_lib.stream_handle())))
     return dq, dk, dv

@@ -318,6 +318,7 @@ size_t seqattn_workspace_size(int op, const seqattn_tensor *q, const seqattn_ten
             return (size_t)(q->b * q->h * q->n * q->d) * sizeof(float);
         return 0;
     case SEQATTN_OP_SEGMENT_BWD:
+    case SEQATTN_OP_DILATED_BWD:
         // D_i = sum_c dO_ic O_ic per query row
         return (size_t)(q->b * q->h * q->n) * sizeof(float);
     default:
@@ -453,8 +454,11 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         return st;
     if (dq->dtype != SEQATTN_F32)
         return fail(SEQATTN_ERR_DTYPE, "dq must be fp32 (accumulated)");
-    if (flags != 0)
+    if (flags & ~SEQATTN_ACCUMULATE)
         return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const bool acc_kv = flags & SEQATTN_ACCUMULATE;
+    if (acc_kv && (dk->dtype != SEQATTN_F32 || dv->dtype != SEQATTN_F32))
+        return fail(SEQATTN_ERR_DTYPE, "dk, dv must be fp32 with SEQATTN_ACCUMULATE");
     const seqattn_tensor *qlike[3] = {o, d_o, dq};
     for (const seqattn_tensor *t : qlike)
         if (t->b != q->b || t->h != q->h || t->n != q->n || t->d != q->d)
@@ -491,8 +495,13 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
     p.dq = view_of(dq);
     p.dk = view_of(dk);
     p.dv = view_of(dv);
-    p.dvec = (float *)workspace;
+    p.dvec.ptr = workspace;
+    p.dvec.sb = q->h * q->n;
+    p.dvec.ss = 0;
+    p.dvec.sh = q->n;
+    p.dvec.sn = 1;
     p.B = (int)q->b;
+    p.S = 1;
     p.Hq = (int)q->h;
     p.Hkv = (int)k->h;
     p.Nq = (int)q->n;
@@ -503,9 +512,160 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
     p.o_f32 = o->dtype == SEQATTN_F32;
     p.dk_f32 = dk->dtype == SEQATTN_F32;
     p.dv_f32 = dv->dtype == SEQATTN_F32;
+    p.acc_kv = acc_kv ? 1 : 0;
     if (p.B == 0 || p.Hkv == 0 || (p.Nk == 0 && p.Nq == 0))
         return ok();
+    hipError_t e = launch_bwd_prep(p, stream_of(hip_stream));
+    if (e != hipSuccess)
+        return hip_status(e, "attn_segment_bwd prep launch");
     return hip_status(launch_bwd_bf16(p, stream_of(hip_stream)), "attn_segment_bwd launch");
+}
+
+int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, const seqattn_tensor *o,
+                             const seqattn_tensor *lse, const seqattn_tensor *d_o,
+                             const int64_t *segment_lengths, const int64_t *dilations,
+                             int32_t n_branches, float softmax_scale, uint32_t flags,
+                             seqattn_tensor *dq, seqattn_tensor *dk, seqattn_tensor *dv,
+                             void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    int st;
+    if ((st = check_qkv(q, k, v, true)))
+        return st;
+    if ((st = check_tensor(o, "o", false)) || (st = check_tensor(lse, "lse", true)) ||
+        (st = check_tensor(d_o, "d_o", false)) || (st = check_tensor(dq, "dq", false)) ||
+        (st = check_tensor(dk, "dk", false)) || (st = check_tensor(dv, "dv", false)))
+        return st;
+    if (q->dtype != SEQATTN_BF16)
+        return fail(SEQATTN_ERR_DTYPE, "dilated attention takes bf16 q/k/v");
+    if (d_o->dtype != SEQATTN_BF16)
+        return fail(SEQATTN_ERR_DTYPE, "d_o must be bf16");
+    if (dq->dtype != SEQATTN_F32 || dk->dtype != SEQATTN_F32 || dv->dtype != SEQATTN_F32)
+        return fail(SEQATTN_ERR_DTYPE, "dq, dk, dv must be fp32");
+    if (!segment_lengths || !dilations)
+        return fail(SEQATTN_ERR_NULL, "segment_lengths / dilations are NULL");
+    if (n_branches < 1 || n_branches > 64)
+        return fail(SEQATTN_ERR_SHAPE, "n_branches must be in [1, 64]");
+    if (flags & ~SEQATTN_CAUSAL)
+        return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    for (int i = 0; i < n_branches; ++i)
+        if (segment_lengths[i] < 1 || dilations[i] < 1 || segment_lengths[i] >= kMaxRows ||
+            dilations[i] >= kMaxRows)
+            return fail(SEQATTN_ERR_SHAPE, "branch %d: w and r must be >= 1", i);
+    const seqattn_tensor *qlike[3] = {o, d_o, dq};
+    for (const seqattn_tensor *t : qlike)
+        if (t->b != q->b || t->h != q->h || t->n != q->n || t->d != q->d)
+            return fail(SEQATTN_ERR_SHAPE, "o, d_o, dq must be [B, Hq, N, d]");
+    if (lse->b != q->b || lse->h != q->h || lse->n != q->n)
+        return fail(SEQATTN_ERR_SHAPE, "lse must be [B, Hq, N, 1]");
+    const seqattn_tensor *klike[2] = {dk, dv};
+    for (const seqattn_tensor *t : klike)
+        if (t->b != k->b || t->h != k->h || t->n != k->n || t->d != k->d)
+            return fail(SEQATTN_ERR_SHAPE, "dk, dv must be [B, Hkv, N, d]");
+    const seqattn_tensor *ins[6] = {q, k, v, o, lse, d_o};
+    const seqattn_tensor *outs[3] = {dq, dk, dv};
+    for (const seqattn_tensor *a : outs) {
+        for (const seqattn_tensor *b : ins)
+            if (overlaps(a, b))
+                return fail(SEQATTN_ERR_ALIAS, "a gradient overlaps an input");
+        for (const seqattn_tensor *b : outs)
+            if (a != b && overlaps(a, b))
+                return fail(SEQATTN_ERR_ALIAS, "gradients overlap each other");
+    }
+    int64_t rmax = 1;
+    for (int i = 0; i < n_branches; ++i)
+        rmax = std::max<int64_t>(rmax, dilations[i]);
+    if ((st = check_head_extent(q, "q", rmax)) || (st = check_head_extent(k, "k", rmax)) ||
+        (st = check_head_extent(v, "v", rmax)) || (st = check_head_extent(d_o, "d_o", rmax)))
+        return st;
+    const size_t need = seqattn_workspace_size(SEQATTN_OP_DILATED_BWD, q, k, n_branches);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(SEQATTN_ERR_WORKSPACE, "need %zu bytes of workspace", need);
+    if (workspace && (uintptr_t)workspace % 16)
+        return fail(SEQATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    const int B = (int)q->b, Hq = (int)q->h, Hkv = (int)k->h, N = (int)q->n, d = (int)q->d;
+    if (B == 0 || N == 0)
+        return ok();
+    hipStream_t s = stream_of(hip_stream);
+    const bool causal = flags & SEQATTN_CAUSAL;
+
+    // D over every query row, from the merged (all-branch) O and dO.
+    BwdParams base;
+    base.q = view_of(q);
+    base.k = view_of(k);
+    base.v = view_of(v);
+    base.o = view_of(o);
+    base.lse = view_of(lse);
+    base.dout = view_of(d_o);
+    base.dq = view_of(dq);
+    base.dk = view_of(dk);
+    base.dv = view_of(dv);
+    base.dvec.ptr = workspace;
+    base.dvec.sb = (int64_t)Hq * N;
+    base.dvec.ss = 0;
+    base.dvec.sh = N;
+    base.dvec.sn = 1;
+    base.B = B;
+    base.S = 1;
+    base.Hq = Hq;
+    base.Hkv = Hkv;
+    base.Nq = base.Nk = N;
+    base.d = d;
+    base.delta = 0;
+    base.noncausal = 1;
+    base.scale = pick_scale(softmax_scale, d);
+    base.o_f32 = o->dtype == SEQATTN_F32;
+    base.dk_f32 = base.dv_f32 = 1;
+    base.acc_kv = 0;
+    hipError_t e = launch_bwd_prep(base, s);
+    if (e != hipSuccess)
+        return hip_status(e, "dilated bwd prep launch");
+
+    // A first branch with r = 1 touches every key row: it writes dK/dV, every
+    // later branch adds to them.  Otherwise they start from zero.
+    const bool first_writes = dilations[0] == 1;
+    if (!first_writes) {
+        if ((e = launch_zero_f32(base.dk, B, Hkv, N, d, s)) != hipSuccess ||
+            (e = launch_zero_f32(base.dv, B, Hkv, N, d, s)) != hipSuccess)
+            return hip_status(e, "dilated bwd init");
+    }
+    for (int i = 0; i < n_branches; ++i) {
+        const int64_t w = std::min<int64_t>(segment_lengths[i], N), r = dilations[i];
+        const int64_t nfull = N / w, tail = N % w;
+        for (int part = 0; part < 2; ++part) {
+            const int64_t nseg = part == 0 ? nfull : (tail > 0 ? 1 : 0);
+            const int64_t seglen = part == 0 ? w : tail;
+            if (nseg == 0)
+                continue;
+            const int64_t row0 = part == 0 ? 0 : nfull * w;
+            const int64_t rows = (seglen + r - 1) / r;
+            // Branch i's selected rows of each segment, as a [B][seg][H][rows] view.
+            auto sub = [&](View vv, int64_t es) {
+                View x = vv;
+                x.ptr = (const char *)vv.ptr + row0 * vv.sn * es;
+                x.ss = w * vv.sn;
+                x.sn = r * vv.sn;
+                return x;
+            };
+            BwdParams p = base;
+            p.q = sub(base.q, 2);
+            p.k = sub(base.k, 2);
+            p.v = sub(base.v, 2);
+            p.lse = sub(base.lse, 4);
+            p.dout = sub(base.dout, 2);
+            p.dq = sub(base.dq, 4);
+            p.dk = sub(base.dk, 4);
+            p.dv = sub(base.dv, 4);
+            p.dvec = sub(base.dvec, 4);
+            p.S = (int)nseg;
+            p.Nq = p.Nk = (int)rows;
+            clamp_delta(causal ? 0 : SEQATTN_NONCAUSAL, rows, rows, &p.delta, &p.noncausal);
+            p.acc_kv = (i == 0 && first_writes) ? 0 : 1;
+            if ((e = launch_bwd_bf16(p, s)) != hipSuccess)
+                return hip_status(e, "dilated bwd branch launch");
+        }
+    }
+    return ok();
 }
 
 }  // extern "C"

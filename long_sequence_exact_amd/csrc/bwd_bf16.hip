@@ -58,18 +58,22 @@ __device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0
 // D_i = sum_c dO_ic O_ic; 16 lanes per row, d/16 elements per lane.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
 {
-    const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+    const int64_t rows = (int64_t)p.B * p.S * p.Hq * p.Nq;
     const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
     const int sub = threadIdx.x & 15;
     const int per = p.d / 16;  // 4 or 8
     float acc = 0.f;
+    int i = 0, h = 0, s = 0, b = 0;
     if (row < rows) {
-        const int i = (int)(row % p.Nq);
-        const int64_t bh = row / p.Nq;
-        const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh +
-                         (int64_t)i * p.dout.sn + sub * per;
-        const int64_t ooff = b * p.o.sb + h * p.o.sh + (int64_t)i * p.o.sn + sub * per;
+        i = (int)(row % p.Nq);
+        int64_t r = row / p.Nq;
+        h = (int)(r % p.Hq);
+        r /= p.Hq;
+        s = (int)(r % p.S);
+        b = (int)(r / p.S);
+        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss +
+                         h * p.dout.sh + (int64_t)i * p.dout.sn + sub * per;
+        const int64_t ooff = b * p.o.sb + s * p.o.ss + h * p.o.sh + (int64_t)i * p.o.sn + sub * per;
         for (int c = 0; c < per; c += 4) {
             const uint2 g = *(const uint2 *)(dO + c);
             float o0, o1, o2, o3;
@@ -87,7 +91,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
     for (int m = 8; m >= 1; m >>= 1)
         acc += __shfl_xor(acc, m, 16);
     if (row < rows && sub == 0)
-        p.dvec[row] = acc;
+        *((float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss + h * p.dvec.sh +
+          (int64_t)i * p.dvec.sn) = acc;
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(View x, int B, int H, int N, int d)
+{
+    const int tpr = d / 4;
+    const int64_t total = (int64_t)B * H * N * tpr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total;
+         gid += stride) {
+        const int64_t row = gid / tpr;
+        const int c4 = (int)(gid % tpr) * 4;
+        const int n = (int)(row % N);
+        const int64_t bh = row / N;
+        const int h = (int)(bh % H), b = (int)(bh / H);
+        *(float4 *)((float *)x.ptr + b * x.sb + h * x.sh + (int64_t)n * x.sn + c4) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 }
 
 template <int D>
@@ -146,14 +168,15 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 
     const int nkt = (p.Nk + kBKV - 1) / kBKV;
     const int kt = (int)(blockIdx.x % nkt);
-    const int bg = (int)(blockIdx.x / nkt);
-    const int g = bg % p.Hkv, b = bg / p.Hkv;
+    const int bsg = (int)(blockIdx.x / nkt);
+    const int g = bsg % p.Hkv, bs = bsg / p.Hkv;
+    const int s = bs % p.S, b = bs / p.S;
     const int k0 = kt * kBKV;
     const int kw0 = k0 + (wave & 3) * 32;
     const int key = kw0 + l32;  // this lane's key (accumulator column)
 
-    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + g * p.k.sh;
-    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + g * p.v.sh;
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh;
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh;
 
     // the wave's K rows (and, for dK, V rows) as B operands (k = d): lane
     // holds key `key`, d = 16kk + 8hl .. +8
@@ -201,8 +224,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     auto prefetch = [&](int it) {
         const int h = g * group + it / per_head;
         const int q0 = (qt_begin + it % per_head) * kBQ;
-        const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + h * p.q.sh;
-        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh;
+        const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh;
+        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss + h * p.dout.sh;
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2);
         const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(p.Nq - 1) * p.dout.sn + D) * 2);
 #pragma unroll
@@ -215,11 +238,12 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             lreg = INFINITY;  // +inf: the row contributes P = 0
             dreg = 0.f;
             if (i < p.Nq) {
-                const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh +
-                                   (int64_t)i * p.lse.sn);
+                const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
+                                   h * p.lse.sh + (int64_t)i * p.lse.sn);
                 if (lv != -INFINITY)
                     lreg = lv * kLog2e;
-                dreg = p.dvec[((int64_t)b * p.Hq + h) * p.Nq + i];
+                dreg = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss +
+                         h * p.dvec.sh + (int64_t)i * p.dvec.sn);
             }
         }
     };
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const View &out = is_dk ? p.dk : p.dv;
     const int out_f32 = is_dk ? p.dk_f32 : p.dv_f32;
     const float f = is_dk ? p.scale : 1.f;
-    const int64_t krow = b * out.sb + g * out.sh + (int64_t)key * out.sn;
+    const int64_t krow = b * out.sb + s * out.ss + g * out.sh + (int64_t)key * out.sn;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -332,7 +356,12 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             const int d0 = i * 32 + gq * 8 + hl * 4;
             const float x0 = acc[i][gq * 4 + 0] * f, x1 = acc[i][gq * 4 + 1] * f;
             const float x2 = acc[i][gq * 4 + 2] * f, x3 = acc[i][gq * 4 + 3] * f;
-            if (out_f32) {
+            if (p.acc_kv) {  // fp32, accumulated
+                float4 *dst = (float4 *)((float *)out.ptr + krow + d0);
+                float4 w = *dst;
+                w.x += x0; w.y += x1; w.z += x2; w.w += x3;
+                *dst = w;
+            } else if (out_f32) {
                 float4 w = {x0, x1, x2, x3};
                 *(float4 *)((float *)out.ptr + krow + d0) = w;
             } else {
@@ -377,16 +406,17 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
     const int gg = lane >> 4, ip = lane & 15;
 
     const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
-    const int BH = p.B * p.Hq;
+    const int BH = p.B * p.S * p.Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // longest first
-    const int bh = (int)(blockIdx.x % BH);
-    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int bsh = (int)(blockIdx.x % BH);
+    const int h = bsh % p.Hq, bs = bsh / p.Hq;
+    const int s = bs % p.S, b = bs / p.S;
     const int g = (int)(((int64_t)h * p.Hkv) / p.Hq);
 
-    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + h * p.q.sh;
-    const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + h * p.dout.sh;
-    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + g * p.k.sh;
-    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + g * p.v.sh;
+    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh;
+    const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss + h * p.dout.sh;
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh;
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2);
     const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(p.Nq - 1) * p.dout.sn + D) * 2);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, ((int64_t)(p.Nk - 1) * p.k.sn + D) * 2);
@@ -411,11 +441,12 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
     }
     float lse2 = INFINITY, dq_d = 0.f;  // +inf: the row contributes P = 0
     if (qrow < p.Nq) {
-        const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh +
-                           (int64_t)qrow * p.lse.sn);
+        const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
+                           h * p.lse.sh + (int64_t)qrow * p.lse.sn);
         if (lv != -INFINITY)
             lse2 = lv * kLog2e;
-        dq_d = p.dvec[((int64_t)b * p.Hq + h) * p.Nq + qrow];
+        dq_d = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss + h * p.dvec.sh +
+                 (int64_t)qrow * p.dvec.sn);
     }
 
     f32x16 acc[D / 32];
@@ -514,7 +545,8 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
 
     if (qrow >= p.Nq)
         return;
-    float *dQ = (float *)p.dq.ptr + b * p.dq.sb + h * p.dq.sh + (int64_t)qrow * p.dq.sn;
+    float *dQ = (float *)p.dq.ptr + b * p.dq.sb + s * p.dq.ss + h * p.dq.sh +
+                (int64_t)qrow * p.dq.sn;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -529,30 +561,49 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
         }
 }
 
+unsigned zero_grid(int64_t threads)
+{
+    int64_t blocks = (threads + 255) / 256;
+    if (blocks > 256 * 64)
+        blocks = 256 * 64;
+    return (unsigned)(blocks > 0 ? blocks : 1);
+}
+
 }  // namespace
+
+hipError_t launch_bwd_prep(const BwdParams &p, hipStream_t st)
+{
+    const int64_t rows = (int64_t)p.B * p.S * p.Hq * p.Nq;
+    if (rows == 0)
+        return hipSuccess;
+    const int64_t blocks = (rows * 16 + 255) / 256;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(const View &x, int B, int H, int N, int d, hipStream_t st)
+{
+    const int64_t threads = (int64_t)B * H * N * (d / 4);
+    if (threads == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(zero_grid(threads)), dim3(256), 0, st, x, B, H, N, d);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st)
 {
-    const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-    if (rows > 0) {
-        const int64_t blocks = (rows * 16 + 255) / 256;
-        hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    const int nkt = (p.Nk + kBKV - 1) / kBKV;
+    const int64_t grid = (int64_t)nkt * p.B * p.S * p.Hkv;
+    if (grid > 0) {
+        if (p.d == 128)
+            hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+        else
+            hipLaunchKernelGGL(bwd_main_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    const int nkt = (p.Nk + kBKV - 1) / kBKV;
-    const int64_t grid = (int64_t)nkt * p.B * p.Hkv;
-    if (grid == 0)
-        return hipSuccess;
-    if (p.d == 128)
-        hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL(bwd_main_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    const int64_t qgrid = (int64_t)((p.Nq + kQBQ - 1) / kQBQ) * p.B * p.Hq;
+    const int64_t qgrid = (int64_t)((p.Nq + kQBQ - 1) / kQBQ) * p.B * p.S * p.Hq;
     if (qgrid == 0 || p.Nk == 0)
         return hipSuccess;
     if (p.d == 128)

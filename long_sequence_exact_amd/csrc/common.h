@@ -33,13 +33,16 @@ struct MergeParams {
     int ob_f32;
 };
 
+// Backward over (query block, KV segment) pairs; like FwdParams, `S` is an
+// extra segment dimension (dilated branches), 1 for a plain segment call.
 struct BwdParams {
     View q, k, v, o, lse, dout, dq, dk, dv;
-    float *dvec;           // workspace: D_i = sum_c dO_ic O_ic, [B*Hq*Nq]
-    int B, Hq, Hkv, Nq, Nk, d;
+    View dvec;             // D_i = sum_c dO_ic O_ic (fp32), same indexing as lse
+    int B, S, Hq, Hkv, Nq, Nk, d;
     int delta, noncausal;
     float scale;
     int o_f32, dk_f32, dv_f32;
+    int acc_kv;            // 1: dk, dv (fp32) are accumulated instead of written
 };
 
 // Launchers (return hipSuccess or the launch error).
@@ -52,6 +55,11 @@ hipError_t launch_fill_empty(const View &o, const View &lse, int B, int S, int H
 // Casts an fp32 [B][H][N][d] view to a bf16 view.
 hipError_t launch_cast_bf16(const View &src, const View &dst, int B, int H, int N,
                             int d, hipStream_t st);
+// D = rowsum(dO o O) over p's [B][S][Hq][Nq] rows into p.dvec.
+hipError_t launch_bwd_prep(const BwdParams &p, hipStream_t st);
+// dK/dV and dQ launches (D must already be in p.dvec).
 hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st);
+// Zero an fp32 [B][H][N][d] view.
+hipError_t launch_zero_f32(const View &x, int B, int H, int N, int d, hipStream_t st);
 
 }  // namespace seqattn

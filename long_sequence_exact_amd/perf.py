@@ -6,7 +6,7 @@ For each synthetic workload the whole hot path is timed with HIP events on
 the launch stream, inputs already resident in HBM:
   ring_16k_bf16       8 ranks x 8 KV segments, fused-merge ring sweep
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
-  longnet_32k_bf16    dilated attention, 5 branches merged by LSE
+  longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
   usp_gqa_256k_bf16   forward sweep over 8 KV blocks, then backward sweep
   lse_merge           standalone merge of two [32, 16384, 128] partials
                       (fp32 accumulator + bf16 partial), reported in GB/s
@@ -20,7 +20,7 @@ import json
 
 import torch
 
-from . import attn_segment_bwd, dilated_attn_fwd, emulate, lse_merge
+from . import attn_segment_bwd, dilated_attn_bwd, dilated_attn_fwd, emulate, lse_merge
 from .synth import WORKLOADS, draw, workload_inputs
 
 PEAK_TFLOPS = 2500.0
@@ -81,7 +81,7 @@ def run(name, reps):
         ms = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=0, out=out, lse=lse), reps)
         fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
     elif name == "longnet_32k_bf16":
-        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
         ms = timed(lambda: dilated_attn_fwd(q, k, v, w.segment_lengths, w.dilations,
@@ -89,6 +89,16 @@ def run(name, reps):
         npairs = sum((w.nq // sl) * (sl // r) ** 2
                      for sl, r in zip(w.segment_lengths, w.dilations))
         fl = 4.0 * w.d * w.hq * npairs
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        ms_b = timed(lambda: dilated_attn_bwd(q, k, v, out, lse, do, w.segment_lengths,
+                                              w.dilations, dq=dq, dk=dk, dv=dv), reps)
+        fl_b = 10.0 * w.d * w.hq * npairs
+        return {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
+                "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl,
+                "bwd_ms": round(ms_b, 3), "bwd_TFLOP/s": round(fl_b / ms_b / 1e9, 1),
+                "bwd_frac_peak": round(fl_b / ms_b / 1e9 / PEAK_TFLOPS, 3)}
     elif name == "usp_gqa_256k_bf16":
         q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
         blk = w.nk // w.segments

@@ -61,3 +61,21 @@ def assert_parity(o, lse, o_ref, lse_ref, dtype, rows_heads=None, what=""):
     assert le <= LSE_TOL, f"{what}: LSE error {le:.3e} > {LSE_TOL}"
     assert same, f"{what}: -inf LSE pattern differs"
     return e, le
+
+
+def dilated_key_list(p, n, ws, rs, causal):
+    """Keys that the dilated branches (w_i, r_i) list for query p, a key once
+    per listing branch: branch i selects p when p's offset in its w_i-segment
+    is a multiple of r_i, and then lists the selected positions of that
+    segment (with causal, those <= p)."""
+    keys = []
+    for w, r in zip(ws, rs):
+        w = min(w, n)
+        s0 = (p // w) * w
+        if (p - s0) % r:
+            continue
+        ks = np.arange(s0, min(s0 + w, n), r)
+        if causal:
+            ks = ks[ks <= p]
+        keys.append(ks)
+    return np.concatenate(keys) if keys else np.zeros(0, np.int64)

@@ -175,7 +175,42 @@ def test_bwd_validation_errors(L):
     assert call(dv_=dv_al) == EALIAS
     dk_bad = T(dk.data, _lib.F32, 1, 2, 511, 128)
     assert call(dk_=dk_bad) == ESHAPE
-    assert call(flags=1) == EUNSUP
+    assert call(flags=4) == EUNSUP
+    dk16 = T(dk.data, _lib.BF16, 1, 2, 512, 128)
+    assert call(dk_=dk16, flags=1) == EDTYPE  # accumulated dK/dV must be fp32
     qf, kf, vf, _, _ = qkvo(dtype=_lib.F32)
     assert L.seqattn_attn_segment_bwd(r(qf), r(kf), r(vf), r(o), r(lse), r(do), 0, 0.0, 0,
                                       r(dq), r(dk), r(dv), ws, need, None) == EUNSUP
+
+
+def test_dilated_bwd_validation_errors(L):
+    r = ctypes.byref
+    step = 1 << 30
+    q, k, v, o, lse = qkvo(hq=4, hkv=2, nq=512, nk=512, d=64, odtype=_lib.F32)
+    do = T(BASE + 5 * step, _lib.BF16, 1, 4, 512, 64)
+    dq = T(BASE + 6 * step, _lib.F32, 1, 4, 512, 64)
+    dk = T(BASE + 7 * step, _lib.F32, 1, 2, 512, 64)
+    dv = T(BASE + 8 * step, _lib.F32, 1, 2, 512, 64)
+    ws = BASE + 9 * step
+    w = (ctypes.c_int64 * 2)(128, 512)
+    rr = (ctypes.c_int64 * 2)(1, 2)
+    need = L.seqattn_workspace_size(_lib.OP_DILATED_BWD, r(q), r(k), 2)
+    assert need == 4 * 512 * 4
+
+    def call(w_=w, r_=rr, nb=2, flags=0, dq_=dq, dk_=dk, dv_=dv, do_=do, ws_=ws, wsb=need):
+        return L.seqattn_dilated_attn_bwd(r(q), r(k), r(v), r(o), r(lse), r(do_), w_, r_, nb,
+                                          0.0, flags, r(dq_), r(dk_), r(dv_), ws_, wsb, None)
+    assert call(nb=0) == ESHAPE
+    assert call(nb=65) == ESHAPE
+    assert call(w_=None) == ENULL
+    assert call(w_=(ctypes.c_int64 * 2)(128, 0)) == ESHAPE
+    assert call(r_=(ctypes.c_int64 * 2)(0, 2)) == ESHAPE
+    assert call(flags=1) == EUNSUP  # only SEQATTN_CAUSAL
+    assert call(wsb=need - 4) == EWS
+    assert call(ws_=None, wsb=0) == EWS
+    assert call(ws_=ws + 4) == EWS  # misaligned
+    assert call(dk_=T(dk.data, _lib.BF16, 1, 2, 512, 64)) == EDTYPE
+    assert call(do_=T(do.data, _lib.F32, 1, 4, 512, 64)) == EDTYPE
+    assert call(dv_=T(dv.data, _lib.F32, 1, 2, 256, 64)) == ESHAPE
+    assert call(dq_=T(dk.data + 512, _lib.F32, 1, 4, 512, 64)) == EALIAS
+    assert call(dv_=T(q.data, _lib.F32, 1, 2, 512, 64)) == EALIAS

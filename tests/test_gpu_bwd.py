@@ -137,6 +137,28 @@ def test_usp_full_size_sampled_and_invariants():
         assert sdk.abs().max() <= 1e-3 * mag
 
 
+def test_bwd_accumulate_kv_over_query_blocks():
+    """Two query blocks against one KV segment (the ring backward, where a KV
+    block's gradient collects every query block's share): the second call
+    adds to dK/dV (SEQATTN_ACCUMULATE); together they equal the full backward."""
+    hq, hkv, nq, nk, d = 4, 2, 320, 256, 128
+    q, k, v, do = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d), (1, hq, nq, d)], 2300)
+    ref = oracle.attn_bwd(_np32(q), _np32(k), _np32(v), _np32(do), delta=0)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = sa.attn_segment_fwd(qd, kd, vd, causal_offset=0, out_dtype=torch.float32)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+    dk = torch.full(k.shape, 5.0, dtype=torch.float32, device=DEV)
+    dv = torch.full(v.shape, 5.0, dtype=torch.float32, device=DEV)
+    cut = 96
+    sa.attn_segment_bwd(qd[..., :cut, :], kd, vd, o[..., :cut, :], lse[..., :cut],
+                        dod[..., :cut, :], causal_offset=0, dq=dq[..., :cut, :], dk=dk, dv=dv)
+    sa.attn_segment_bwd(qd[..., cut:, :], kd, vd, o[..., cut:, :], lse[..., cut:],
+                        dod[..., cut:, :], causal_offset=cut, dq=dq[..., cut:, :], dk=dk, dv=dv,
+                        accumulate_kv=True)
+    torch.cuda.synchronize()
+    _grads_parity(dq, dk, dv, ref, "bwd accumulate_kv")
+
+
 def test_bwd_sequence_major_layout_views():
     """Backward on [B, N, H, d]-stored tensors passed as permuted views."""
     B, N, H, Hkv, d, delta = 1, 300, 4, 2, 128, 0

@@ -509,3 +509,32 @@ def test_dilated_bwd_invariants():
     _, dk, dv = oracle.dilated_bwd(q, k, v, do, (16, 32, 64), (1, 2, 4), causal=True)
     assert np.abs(dv.sum(axis=2)[0, 0] - do.astype(np.float64).sum(axis=(1, 2))[0]).max() < 1e-12
     assert np.abs(dk.sum(axis=2)).max() < 1e-12
+
+
+@pytest.mark.parametrize("ws,rs,causal", [
+    ((16, 40, 100), (1, 3, 8), True),     # tails, dilations not dividing w
+    ((24, 96), (2, 4), False),            # odd positions unselected
+])
+def test_dilated_bwd_dq_equals_segment_bwd_over_listed_keys(ws, rs, causal):
+    # The full-size GPU check of dilated dQ runs the segment backward on each
+    # sampled row's listed keys (repeated once per listing branch); on small
+    # inputs that equals the dilated backward row by row, and the listing
+    # agrees with the multiplicity matrix.
+    from tests.parity import dilated_key_list
+    n, d = 90, 8
+    q = _rand((1, 2, n, d), 430)
+    k = _rand((1, 1, n, d), 431)
+    v = _rand((1, 1, n, d), 432)
+    do = _rand((1, 2, n, d), 433)
+    dq, _, _ = oracle.dilated_bwd(q, k, v, do, ws, rs, causal=causal)
+    c = _multiplicity(n, ws, rs, causal)
+    for p in range(n):
+        keys = dilated_key_list(p, n, ws, rs, causal)
+        assert np.array_equal(np.bincount(keys, minlength=n), c[p])
+        for h in range(2):
+            if len(keys) == 0:
+                assert np.all(dq[0, h, p] == 0)
+                continue
+            ref, _, _ = oracle.attn_bwd_dq_rows(q[0, h:h + 1, p:p + 1], k[0][:, keys],
+                                                v[0][:, keys], do[0, h:h + 1, p:p + 1])
+            assert np.abs(ref[0] - dq[0, h, p]).max() < 1e-12 * max(1.0, np.abs(ref).max())
