@@ -14,6 +14,11 @@ block, KV segment) pairs are issued, in which order, with which offset.
   on the GPU's head subset at full length.
 * USP ("Boosting Spec Eagle ...", The Solution: Ulysses and Ring combined):
   a head subset swept over KV blocks like a ring rank, forward and backward.
+* Load-balanced causal ring ("Boosting Spec Eagle ...", The Solution: the
+  ring's per-step work; the plain causal ring leaves rank r idle for the
+  P-1-r steps whose KV block lies in its future).  The sequence is cut into
+  2P chunks and rank r holds chunks r and 2P-1-r, so every step gives every
+  rank the same number of visible pairs.
 """
 from __future__ import annotations
 
@@ -52,22 +57,27 @@ def sweep_fwd(q, k, v, n_blocks: int, q_block: int, causal: bool, out, lse, scal
                          out=out, lse=lse, accumulate=not first)
         first = False
         launches += 1
-    if first:  # nothing visible at all
-        out.zero_()
-        lse.fill_(float("-inf"))
+    if first:  # nothing visible at all: the empty segment writes (0, -inf)
+        attn_segment_fwd(q, k[..., :0, :], v[..., :0, :], scale=scale, out=out, lse=lse)
+        launches += 1
     return launches
 
 
-def _blocks(t, P, blk, first_block, count):
-    """View of `count` consecutive length-blk row blocks of t ([1,H,N,d] or
-    [1,H,N]) starting at block `first_block`, as a batch: [count, H, blk(, d)]."""
+def _rows_batch(t, row0, rows, step, count):
+    """View of `count` row ranges [row0 + c*step, row0 + c*step + rows) of t
+    ([1,H,N,d] or [1,H,N]) as a batch: [count, H, rows(, d)]."""
     st = t.stride()
+    off = t.storage_offset() + row0 * st[2]
     if t.dim() == 4:
-        return t.as_strided((count, t.shape[1], blk, t.shape[3]),
-                            (blk * st[2], st[1], st[2], st[3]),
-                            t.storage_offset() + first_block * blk * st[2])
-    return t.as_strided((count, t.shape[1], blk), (blk * st[2], st[1], st[2]),
-                        t.storage_offset() + first_block * blk * st[2])
+        return t.as_strided((count, t.shape[1], rows, t.shape[3]),
+                            (step * st[2], st[1], st[2], st[3]), off)
+    return t.as_strided((count, t.shape[1], rows), (step * st[2], st[1], st[2]), off)
+
+
+def _blocks(t, P, blk, first_block, count):
+    """View of `count` consecutive length-blk row blocks of t starting at
+    block `first_block`, as a batch: [count, H, blk(, d)]."""
+    return _rows_batch(t, first_block * blk, blk, blk, count)
 
 
 def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True):
@@ -102,6 +112,68 @@ def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = T
                              _blocks(v, P, blk, j0, cnt), causal_offset=delta, scale=scale,
                              out=_blocks(out, P, blk, r0, cnt), lse=_blocks(lse, P, blk, r0, cnt),
                              accumulate=t > 0)
+    return out, lse
+
+
+def zigzag_order(n: int, P: int):
+    """Global row of each row of the zigzag layout: rank r's 2n/(2P) rows are
+    chunk r followed by chunk 2P-1-r of the sequence (chunks of n/(2P) rows)."""
+    c = n // (2 * P)
+    rows = []
+    for r in range(P):
+        rows.extend(range(r * c, (r + 1) * c))
+        rows.extend(range((2 * P - 1 - r) * c, (2 * P - r) * c))
+    return rows
+
+
+def zigzag_plan(n: int, P: int):
+    """Launches of the zigzag causal ring over P ranks (zigzag layout rows).
+
+    Each launch is (step, q_rows, kv_rows, causal_offset, accumulate), where
+    q_rows / kv_rows = (row0, rows, count) name `count` row ranges
+    [row0 + i*2c, row0 + i*2c + rows), c = n/(2P), one per rank of the batch.
+
+    Step 0: every rank attends to its own two chunks; in rank-local order the
+    causal rule between them is plain j <= i (chunk r precedes chunk 2P-1-r),
+    so that is one causal launch over all ranks.  Step t > 0: rank r holds
+    the KV of rank j = (r - t) mod P.  For j < r both of r's chunks see all of
+    chunk j and none of chunk 2P-1-j; for j > r only r's second chunk sees
+    anything, and it sees both of j's chunks.  Each case is one non-causal
+    launch over its ranks, and every rank gets 2c^2 pairs per step.
+    """
+    if n % (2 * P):
+        raise ValueError("zigzag ring needs N divisible by 2P")
+    c = n // (2 * P)
+    plan = [(0, (0, 2 * c, P), (0, 2 * c, P), 0, False)]
+    for t in range(1, P):
+        # ranks r = t..P-1 hold j = r - t < r: all 2c rows vs j's first chunk
+        plan.append((t, (2 * c * t, 2 * c, P - t), (0, c, P - t), None, True))
+        # ranks r = 0..t-1 hold j = r - t + P > r: second chunk vs both of j's
+        plan.append((t, (c, c, t), (2 * c * (P - t), 2 * c, t), None, True))
+    return plan
+
+
+def zigzag_ring_fwd(q, k, v, P: int, scale=None, out=None, lse=None):
+    """Causal ring over P ranks with the zigzag split, all ranks on one GPU.
+
+    q, k, v: [1,H,N,d] in the zigzag layout (zigzag_order; rank r owns rows
+    [r*2c, (r+1)*2c)).  Returns the merged fp32 output and LSE in the same
+    layout.  Issues the launches of zigzag_plan.
+    """
+    _, H, n, d = q.shape
+    if q.shape[0] != 1:
+        raise ValueError("zigzag ring takes B = 1")
+    plan = zigzag_plan(n, P)
+    step = n // P
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    for _, (q0, qn, cnt), (k0, kn, _), delta, acc in plan:
+        attn_segment_fwd(_rows_batch(q, q0, qn, step, cnt), _rows_batch(k, k0, kn, step, cnt),
+                         _rows_batch(v, k0, kn, step, cnt), causal_offset=delta, scale=scale,
+                         out=_rows_batch(out, q0, qn, step, cnt),
+                         lse=_rows_batch(lse, q0, qn, step, cnt), accumulate=acc)
     return out, lse
 
 
@@ -141,10 +213,8 @@ def usp_bwd(q, k, v, out, lse, d_o, n_blocks: int, q_block: int, causal: bool = 
         k_start = j * blk
         rows = slice(k_start, k_start + blk)
         delta = q_start - k_start
-        if causal and delta + q.shape[-2] - 1 < 0:
-            dk[..., rows, :].zero_()
-            dv[..., rows, :].zero_()
-            continue
+        # a block wholly in the causal future still gets its call: the kernel
+        # finds no visible pair and writes dK = dV = 0
         attn_segment_bwd(q, k[..., rows, :], v[..., rows, :], out, lse, d_o,
                          causal_offset=delta if causal else None, scale=scale, dq=dq,
                          dk=dk[..., rows, :], dv=dv[..., rows, :])

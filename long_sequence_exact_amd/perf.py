@@ -5,13 +5,16 @@
 For each synthetic workload the whole hot path is timed with HIP events on
 the launch stream, inputs already resident in HBM:
   ring_16k_bf16       8 ranks x 8 KV segments, fused-merge ring sweep
+  ring_16k_bf16_zigzag  the same with the load-balanced zigzag split
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
   usp_gqa_256k_bf16   forward sweep over 8 KV blocks, then backward sweep
   lse_merge           standalone merge of two [32, 16384, 128] partials
                       (fp32 accumulator + bf16 partial), reported in GB/s
 FLOPs are algorithmic (4*d per visible pair forward, 10*d backward); bytes
-for the merge are the tensors read and written.
+for the merge are the tensors read and written.  The ring lines also time
+every (rank, step) call alone, as on a device of its own, and report the
+critical path (sum over steps of the slowest rank) and the load balance.
 """
 from __future__ import annotations
 
@@ -20,7 +23,8 @@ import json
 
 import torch
 
-from . import attn_segment_bwd, dilated_attn_bwd, dilated_attn_fwd, emulate, lse_merge
+from . import (attn_segment_bwd, attn_segment_fwd, dilated_attn_bwd, dilated_attn_fwd,
+               emulate, lse_merge)
 from .synth import WORKLOADS, draw, workload_inputs
 
 PEAK_TFLOPS = 2500.0
@@ -56,6 +60,47 @@ def timed(fn, reps, warmup=2):
     return a.elapsed_time(b) / reps
 
 
+def ring_critical_path(q, k, v, P, zigzag, reps):
+    """Per-rank timing of a causal ring: each (rank, step) call runs alone on
+    the GPU (as it would on its own device) and is timed with HIP events.
+
+    Returns (critical-path ms = sum over steps of the slowest rank's call,
+    mean per-rank busy ms).  Their ratio is the ring's load balance; transfers
+    between ranks are not modelled.
+    """
+    n = q.shape[-2]
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    calls = {}  # (rank, step) -> list of thunks
+    if zigzag:
+        step_rows = n // P
+        for t, (q0, qn, cnt), (k0, kn, _), delta, acc in emulate.zigzag_plan(n, P):
+            for b in range(cnt):
+                qs = slice(q0 + b * step_rows, q0 + b * step_rows + qn)
+                ks = slice(k0 + b * step_rows, k0 + b * step_rows + kn)
+                rank = (q0 + b * step_rows) // step_rows
+                calls.setdefault((rank, t), []).append(
+                    lambda qs=qs, ks=ks, delta=delta, acc=acc: attn_segment_fwd(
+                        q[..., qs, :], k[..., ks, :], v[..., ks, :], causal_offset=delta,
+                        out=out[..., qs, :], lse=lse[..., qs], accumulate=acc))
+    else:
+        blk = n // P
+        for r in range(P):
+            for t, j in enumerate(emulate.ring_order(r, P)):
+                delta = (r - j) * blk
+                if delta + blk - 1 < 0:
+                    continue
+                qs, ks = slice(r * blk, (r + 1) * blk), slice(j * blk, (j + 1) * blk)
+                calls.setdefault((r, t), []).append(
+                    lambda qs=qs, ks=ks, delta=delta, t=t: attn_segment_fwd(
+                        q[..., qs, :], k[..., ks, :], v[..., ks, :], causal_offset=delta,
+                        out=out[..., qs, :], lse=lse[..., qs], accumulate=t > 0))
+    ms = {key: timed(lambda fns=fns: [f() for f in fns], reps) for key, fns in calls.items()}
+    crit = sum(max(ms.get((r, t), 0.0) for r in range(P)) for t in range(P))
+    busy = sum(ms.values()) / P
+    return crit, busy
+
+
 def run(name, reps):
     dev = "cuda"
     if name == "lse_merge":
@@ -68,16 +113,25 @@ def run(name, reps):
         nbytes = oa.numel() * 4 * 2 + ob.numel() * 2 + la.numel() * 4 * 2 + lb.numel() * 4
         return {"workload": name, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
                 "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_GBS, 3), "bytes": nbytes}
-    w = WORKLOADS[name]
+    w = WORKLOADS.get(name)
     if name == "ring_16k_bf16":
         q, k, v = (t.to(dev) for t in workload_inputs(w))
         ms = timed(lambda: emulate.ring_fwd(q, k, v, w.segments, causal=True), reps)
         fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
+        crit, busy = ring_critical_path(q, k, v, w.segments, False, reps)
+    elif name == "ring_16k_bf16_zigzag":
+        w = WORKLOADS["ring_16k_bf16"]
+        order = torch.tensor(emulate.zigzag_order(w.nq, w.segments), device=dev)
+        q, k, v = (t.to(dev)[:, :, order].contiguous() for t in workload_inputs(w))
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        ms = timed(lambda: emulate.zigzag_ring_fwd(q, k, v, w.segments, out=out, lse=lse), reps)
+        fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
+        crit, busy = ring_critical_path(q, k, v, w.segments, True, reps)
     elif name == "ulysses_128k_bf16":
         q, k, v = (t.to(dev) for t in workload_inputs(w))
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-        from . import attn_segment_fwd
         ms = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=0, out=out, lse=lse), reps)
         fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
     elif name == "longnet_32k_bf16":
@@ -121,14 +175,21 @@ def run(name, reps):
                 "bwd_frac_peak": round(fl_b / ms_b / 1e9 / PEAK_TFLOPS, 3)}
     else:
         raise ValueError(name)
-    return {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
-            "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl}
+    res = {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
+           "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl}
+    if name.startswith("ring_16k"):
+        # one device per rank: per-step slowest rank, summed over the steps
+        res.update({"rank_critical_path_ms": round(crit, 3),
+                    "rank_mean_busy_ms": round(busy, 3),
+                    "rank_balance": round(busy / crit, 3)})
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", nargs="*",
-                    default=["ulysses_128k_bf16", "ring_16k_bf16", "longnet_32k_bf16",
+                    default=["ulysses_128k_bf16", "ring_16k_bf16", "ring_16k_bf16_zigzag",
+                             "longnet_32k_bf16",
                              "usp_gqa_256k_bf16", "lse_merge"])
     ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()

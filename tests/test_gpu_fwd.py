@@ -177,6 +177,21 @@ def test_ring_sweep_matches_full_causal_attention_small():
     assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="ring small")
 
 
+@pytest.mark.parametrize("P,c,H,d", [(4, 96, 2, 128), (3, 70, 2, 64), (1, 128, 1, 128)])
+def test_zigzag_ring_matches_full_causal_attention_small(P, c, H, d):
+    n = 2 * P * c
+    q, k, v = draw([(1, H, n, d)] * 3, 45 + P)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=0)
+    order = torch.tensor(emulate.zigzag_order(n, P))
+    oz, lz = emulate.zigzag_ring_fwd(*(t[:, :, order].to(DEV) for t in (q, k, v)), P)
+    torch.cuda.synchronize()
+    o = torch.empty(oz.shape, dtype=oz.dtype)
+    lse = torch.empty(lz.shape, dtype=lz.dtype)
+    o[:, :, order] = oz.cpu()
+    lse[:, :, order] = lz.cpu()
+    assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="zigzag ring small")
+
+
 def _sampled_check(q, k, v, o, lse, delta, rows_per_head, seed, must_rows=(0, -1)):
     """Oracle on a seeded row subset of every head; compare the GPU rows."""
     B, H, N, d = q.shape
@@ -201,6 +216,24 @@ def test_ring_16k_full_size_sampled():
     og, lg, orf, lrf, heads = _sampled_check(q, k, v, o, lse, 0, 24, 1000 + w.seed,
                                              must_rows=(0, 2047, 2048, w.nq - 1))
     assert_parity(og, lg, orf, lrf, torch.bfloat16, rows_heads=heads, what="ring 16k")
+
+
+def test_zigzag_ring_16k_full_size_sampled():
+    """The ring workload (32 heads, d=128, 16384 tokens, causal, 8 ranks) with
+    the zigzag split; sampled rows (in sequence order) against the oracle."""
+    w = WORKLOADS["ring_16k_bf16"]
+    q, k, v = workload_inputs(w)
+    order = torch.tensor(emulate.zigzag_order(w.nq, w.segments))
+    oz, lz = emulate.zigzag_ring_fwd(*(t.to(DEV)[:, :, order.to(DEV)] for t in (q, k, v)),
+                                     w.segments)
+    torch.cuda.synchronize()
+    o = torch.empty(oz.shape, dtype=oz.dtype)
+    lse = torch.empty(lz.shape, dtype=lz.dtype)
+    o[:, :, order] = oz.cpu()
+    lse[:, :, order] = lz.cpu()
+    og, lg, orf, lrf, heads = _sampled_check(q, k, v, o, lse, 0, 24, 1100 + w.seed,
+                                             must_rows=(0, 1023, 1024, w.nq - 1024, w.nq - 1))
+    assert_parity(og, lg, orf, lrf, torch.bfloat16, rows_heads=heads, what="zigzag ring 16k")
 
 
 def test_ulysses_128k_full_size_sampled():

@@ -5,7 +5,9 @@ import pytest
 import torch
 
 from bench import visible_pairs
-from long_sequence_exact_amd.emulate import ring_order
+import numpy as np
+
+from long_sequence_exact_amd.emulate import ring_order, zigzag_order, zigzag_plan
 from long_sequence_exact_amd.synth import WORKLOADS, draw, sample_rows
 
 
@@ -39,6 +41,35 @@ def test_ring_schedule_covers_causal_attention_exactly():
             pairs += visible_pairs(blk, blk, delta)
     assert calls == 36
     assert pairs == visible_pairs(P * blk, P * blk, 0) == 134_225_920
+
+
+@pytest.mark.parametrize("n,P", [(16, 1), (32, 2), (48, 4), (64, 8)])
+def test_zigzag_plan_covers_causal_attention_once_and_balances_ranks(n, P):
+    """Every causal (query, key) pair of the sequence is issued exactly once,
+    no non-causal pair is issued, and each step gives every rank the same
+    number of pairs (step 0: c(c+1) + c^2; later steps: 2c^2)."""
+    order = np.array(zigzag_order(n, P))
+    assert sorted(order) == list(range(n))
+    c, step = n // (2 * P), n // P
+    hits = np.zeros((n, n), np.int64)
+    per_rank_step = np.zeros((P, P), np.int64)
+    for t, (q0, qn, cnt), (k0, kn, kcnt), delta, acc in zigzag_plan(n, P):
+        assert cnt == kcnt and acc == (t > 0)
+        for b in range(cnt):
+            qrows = q0 + b * step + np.arange(qn)
+            krows = k0 + b * step + np.arange(kn)
+            rank = int(qrows[0] // step)
+            assert (qrows // step == rank).all()
+            assert int(krows[0] // step) == (rank - t) % P  # the ring's KV holder
+            for i, gi in enumerate(order[qrows]):
+                for j, gj in enumerate(order[krows]):
+                    if delta is None or j <= i + delta:
+                        hits[gi, gj] += 1
+                        per_rank_step[rank, t] += 1
+    assert np.array_equal(hits, np.tril(np.ones((n, n), np.int64)))
+    assert (per_rank_step[:, 0] == c * (c + 1) + c * c).all()
+    assert (per_rank_step[:, 1:] == 2 * c * c).all()
+    assert len(zigzag_plan(n, P)) == 2 * P - 1
 
 
 def test_usp_share_pairs():
