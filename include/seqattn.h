@@ -231,6 +231,27 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              seqattn_tensor *dv, void *workspace,
                              size_t workspace_bytes, void *hip_stream);
 
+/*
+ * seqattn_head_relayout -- copy every (head, row) vector of src into dst,
+ * where the two describe the same heads in different strided layouts.
+ *
+ * Passage: "DeepSpeed-Ulysses" article, Wie DeepSpeed-Ulysses funktioniert
+ * (the sequence is split across GPUs; an all-to-all before attention gives
+ * each GPU the whole sequence, and after attention the results are gathered
+ * and re-organised).  The re-layouts on either side of that all-to-all are
+ * this copy: a rank's [Ns, H, d] shard, seen as b = 1, h = H, n = Ns, goes
+ * to its [P][Ns][H/P][d] send buffer, seen as b = P, h = H/P, n = Ns, and
+ * back after attention.
+ *
+ * Flat heads f = b * h + h_index enumerate both sides (src->b * src->h ==
+ * dst->b * dst->h); n, d and dtype match; dst[f][row] = src[f][row].
+ * d * element size must be a multiple of 16 bytes, dst rows must not
+ * overlap each other or src, and one call moves fewer than 2^31 16-byte units.
+ * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, UNSUPPORTED, HIP.
+ */
+int seqattn_head_relayout(const seqattn_tensor *src, seqattn_tensor *dst,
+                          void *hip_stream);
+
 /* Bytes of device workspace an op needs for these operands (0 if none).
  * For SEQATTN_OP_DILATED_FWD pass o's descriptor as `k`. */
 size_t seqattn_workspace_size(int op, const seqattn_tensor *q,

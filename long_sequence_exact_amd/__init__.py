@@ -9,6 +9,7 @@ torch's current stream.  All computation happens in the library's kernels.
     dilated_attn_fwd(q, k, v, segment_lengths, dilations, causal=False) -> (o, lse)
     attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, ...) -> (dq, dk, dv)
     dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, ...) -> (dq, dk, dv)
+    head_relayout(src, dst)                             (dst[f][n] = src[f][n])
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ from . import _lib
 from ._lib import ACCUMULATE, CAUSAL, NONCAUSAL, SeqattnError
 
 __all__ = ["attn_segment_fwd", "lse_merge", "dilated_attn_fwd", "attn_segment_bwd",
-           "dilated_attn_bwd", "workspace_size", "NONCAUSAL", "SeqattnError", "version"]
+           "dilated_attn_bwd", "head_relayout", "workspace_size", "NONCAUSAL", "SeqattnError", "version"]
 
 
 def version() -> int:
@@ -170,3 +171,14 @@ def dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, causal=Fa
         ctypes.byref(gv), ctypes.c_void_p(wptr), wbytes,
         ctypes.c_void_p(_lib.stream_handle())))
     return dq, dk, dv
+
+
+def head_relayout(src, dst):
+    """Copy each (flat head, row) vector of src into dst: two [B,H,N,d] views
+    of the same B*H heads in different layouts (the re-layouts around the
+    Ulysses all-to-all)."""
+    L = _lib.lib()
+    a, b = _lib.desc(src), _lib.desc(dst)
+    _lib.check(L.seqattn_head_relayout(ctypes.byref(a), ctypes.byref(b),
+                                       ctypes.c_void_p(_lib.stream_handle())))
+    return dst

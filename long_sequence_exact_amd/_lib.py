@@ -22,8 +22,9 @@ CAUSAL = 2
 OP_SEGMENT_FWD, OP_LSE_MERGE, OP_DILATED_FWD, OP_SEGMENT_BWD, OP_DILATED_BWD = 0, 1, 2, 3, 4
 
 EXPORTS = ("seqattn_attn_segment_fwd", "seqattn_lse_merge", "seqattn_dilated_attn_fwd",
-           "seqattn_attn_segment_bwd", "seqattn_dilated_attn_bwd", "seqattn_workspace_size",
-           "seqattn_status_string", "seqattn_last_error", "seqattn_version")
+           "seqattn_attn_segment_bwd", "seqattn_dilated_attn_bwd", "seqattn_head_relayout",
+           "seqattn_workspace_size", "seqattn_status_string", "seqattn_last_error",
+           "seqattn_version")
 
 
 class Tensor(ctypes.Structure):
@@ -63,13 +64,15 @@ def lib():
     L.seqattn_dilated_attn_bwd.argtypes = [P, P, P, P, P, P, ctypes.POINTER(I64),
                                            ctypes.POINTER(I64), ctypes.c_int32, F, U32, P, P,
                                            P, VP, ctypes.c_size_t, VP]
+    L.seqattn_head_relayout.argtypes = [P, P, VP]
     L.seqattn_workspace_size.argtypes = [ctypes.c_int, P, P, ctypes.c_int32]
     L.seqattn_workspace_size.restype = ctypes.c_size_t
     L.seqattn_status_string.restype = ctypes.c_char_p
     L.seqattn_status_string.argtypes = [ctypes.c_int]
     L.seqattn_last_error.restype = ctypes.c_char_p
     for f in ("seqattn_attn_segment_fwd", "seqattn_lse_merge", "seqattn_dilated_attn_fwd",
-              "seqattn_attn_segment_bwd", "seqattn_dilated_attn_bwd", "seqattn_version"):
+              "seqattn_attn_segment_bwd", "seqattn_dilated_attn_bwd", "seqattn_head_relayout",
+              "seqattn_version"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

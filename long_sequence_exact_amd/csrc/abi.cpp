@@ -105,6 +105,28 @@ bool overlaps(const seqattn_tensor *a, const seqattn_tensor *b)
     return al < bh && bl < ah;
 }
 
+// An output's (b, h, n) rows must not overlap each other (else the writes of
+// different rows race).  Sufficient test: with the dimensions of size > 1
+// sorted by stride, each stride is at least the extent of the ones before.
+int check_distinct_rows(const seqattn_tensor *t, const char *name)
+{
+    if (numel(t) == 0)
+        return SEQATTN_OK;
+    struct Dim {
+        int64_t size, stride;
+    } dims[3] = {{t->b, t->stride_b}, {t->h, t->stride_h}, {t->n, t->stride_n}};
+    std::sort(dims, dims + 3, [](const Dim &x, const Dim &y) { return x.stride < y.stride; });
+    int64_t extent = t->d;
+    for (const Dim &dm : dims) {
+        if (dm.size <= 1)
+            continue;
+        if (dm.stride < extent)
+            return fail(SEQATTN_ERR_STRIDE, "%s: strides make rows overlap", name);
+        extent = dm.stride * (dm.size - 1) + extent;
+    }
+    return SEQATTN_OK;
+}
+
 View view_of(const seqattn_tensor *t)
 {
     View v;
@@ -181,6 +203,8 @@ int check_out(const seqattn_tensor *o, const seqattn_tensor *lse, const seqattn_
             return fail(SEQATTN_ERR_ALIAS, "outputs overlap an input");
     if (overlaps(o, lse))
         return fail(SEQATTN_ERR_ALIAS, "o and lse overlap");
+    if ((st = check_distinct_rows(o, "o")) || (st = check_distinct_rows(lse, "lse")))
+        return st;
     return SEQATTN_OK;
 }
 
@@ -292,6 +316,8 @@ int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
     if (overlaps(o_acc, o_b) || overlaps(o_acc, lse_b) || overlaps(lse_acc, o_b) ||
         overlaps(lse_acc, lse_b) || overlaps(o_acc, lse_acc))
         return fail(SEQATTN_ERR_ALIAS, "accumulator overlaps the merged partial");
+    if ((st = check_distinct_rows(o_acc, "o_acc")) || (st = check_distinct_rows(lse_acc, "lse_acc")))
+        return st;
     MergeParams p;
     p.oa = view_of(o_acc);
     p.la = view_of(lse_acc);
@@ -478,6 +504,8 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         for (const seqattn_tensor *b : outs)
             if (a != b && overlaps(a, b))
                 return fail(SEQATTN_ERR_ALIAS, "gradients overlap each other");
+        if ((st = check_distinct_rows(a, "gradient")))
+            return st;
     }
     const size_t need = seqattn_workspace_size(SEQATTN_OP_SEGMENT_BWD, q, k, 0);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -571,6 +599,8 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         for (const seqattn_tensor *b : outs)
             if (a != b && overlaps(a, b))
                 return fail(SEQATTN_ERR_ALIAS, "gradients overlap each other");
+        if ((st = check_distinct_rows(a, "gradient")))
+            return st;
     }
     int64_t rmax = 1;
     for (int i = 0; i < n_branches; ++i)
@@ -666,6 +696,50 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         }
     }
     return ok();
+}
+
+int seqattn_head_relayout(const seqattn_tensor *src, seqattn_tensor *dst, void *hip_stream)
+{
+    int st;
+    if ((st = check_tensor(src, "src", false)) || (st = check_tensor(dst, "dst", false)))
+        return st;
+    if (src->dtype != dst->dtype)
+        return fail(SEQATTN_ERR_DTYPE, "src and dst dtypes differ");
+    if (src->n != dst->n || src->d != dst->d || src->b * src->h != dst->b * dst->h)
+        return fail(SEQATTN_ERR_SHAPE, "src and dst must hold the same b*h heads of n rows of d");
+    const int64_t row_bytes = src->d * esize(src->dtype);
+    if (row_bytes % 16)
+        return fail(SEQATTN_ERR_SHAPE, "d * element size must be a multiple of 16 bytes");
+    const int64_t heads = src->b * src->h;
+    if (heads == 0 || src->n == 0 || src->d == 0)
+        return ok();
+    if ((row_bytes / 16) * heads * src->n >= ((int64_t)1 << 31))
+        return fail(SEQATTN_ERR_UNSUPPORTED, "more than 2^31 16-byte units in one call");
+    if (src->h == 0 || dst->h == 0)
+        return fail(SEQATTN_ERR_SHAPE, "h must be positive");
+    if (overlaps(src, dst))
+        return fail(SEQATTN_ERR_ALIAS, "dst overlaps src");
+    if ((st = check_distinct_rows(dst, "dst")))
+        return st;
+    const int es = esize(src->dtype);
+    RelayoutParams p;
+    p.src = (const char *)src->data;
+    p.dst = (char *)dst->data;
+    p.s_sb = src->stride_b * es;
+    p.s_sh = src->stride_h * es;
+    p.s_sn = src->stride_n * es;
+    p.d_sb = dst->stride_b * es;
+    p.d_sh = dst->stride_h * es;
+    p.d_sn = dst->stride_n * es;
+    p.src_h = (uint32_t)src->h;
+    p.dst_h = (uint32_t)dst->h;
+    p.F = (uint32_t)heads;
+    p.N = (uint32_t)src->n;
+    p.units = (uint32_t)(row_bytes / 16);
+    // lanes walk the source's faster-moving of (head, row)
+    const int64_t src_head_stride = src->h > 1 ? src->stride_h : src->stride_b;
+    p.head_fast = (heads > 1 && src->n > 1 && src_head_stride < src->stride_n) ? 1 : 0;
+    return hip_status(launch_head_relayout(p, stream_of(hip_stream)), "head_relayout launch");
 }
 
 }  // extern "C"

@@ -45,6 +45,18 @@ struct BwdParams {
     int acc_kv;            // 1: dk, dv (fp32) are accumulated instead of written
 };
 
+// Copy of (flat head f, row n) vectors between two strided layouts; strides
+// in bytes, a vector is `units` 16-byte units.  f = b * src_h + h on the
+// source side and b * dst_h + h on the destination side.
+struct RelayoutParams {
+    const char *src;
+    char *dst;
+    int64_t s_sb, s_sh, s_sn;
+    int64_t d_sb, d_sh, d_sn;
+    uint32_t src_h, dst_h, F, N, units;
+    int head_fast;  // 1: consecutive lanes walk heads of one row, 0: rows of one head
+};
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t st);
@@ -61,5 +73,6 @@ hipError_t launch_bwd_prep(const BwdParams &p, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st);
 // Zero an fp32 [B][H][N][d] view.
 hipError_t launch_zero_f32(const View &x, int B, int H, int N, int d, hipStream_t st);
+hipError_t launch_head_relayout(const RelayoutParams &p, hipStream_t st);
 
 }  // namespace seqattn

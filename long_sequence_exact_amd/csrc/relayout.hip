@@ -1,0 +1,72 @@
+// Head regroup copy: the re-layout that flanks the Ulysses all-to-all.
+//
+// "DeepSpeed-Ulysses" article, Wie DeepSpeed-Ulysses funktioniert: the input
+// is split along the sequence across GPUs; an all-to-all before attention
+// gives every GPU the whole sequence (for its share of the heads), and the
+// results are collected and re-organised afterwards.  Each side of that
+// exchange moves whole (head, row) vectors of d elements between two strided
+// layouts that enumerate the same flat heads f = b * h_count + h (for
+// example a rank's [Ns][H][d] shard and its [P][Ns][H/P][d] send buffer).
+// The copy is HBM-bound: every thread moves 16-byte units, consecutive lanes
+// take consecutive units of one vector, and the flat-head / row order of
+// the lanes follows whichever of the two source strides is smaller, so both
+// sides are read and written in runs of at least one vector.
+#include "common.h"
+
+namespace seqattn {
+namespace {
+
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(256) void head_relayout_kernel(const RelayoutParams p)
+{
+    const uint32_t total = p.units * p.F * p.N;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < total;
+         base += kUnroll * stride) {
+        uint4 x[kUnroll];
+        int64_t dst_off[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t u = base + k * stride;
+            dst_off[k] = -1;
+            if (u >= total)
+                continue;
+            const uint32_t c = u % p.units;
+            const uint32_t r = u / p.units;
+            uint32_t f, n;
+            if (p.head_fast) {
+                f = r % p.F;
+                n = r / p.F;
+            } else {
+                n = r % p.N;
+                f = r / p.N;
+            }
+            const uint32_t sb = f / p.src_h, sh = f % p.src_h;
+            const uint32_t db = f / p.dst_h, dh = f % p.dst_h;
+            const int64_t so = sb * p.s_sb + sh * p.s_sh + (int64_t)n * p.s_sn + c * 16;
+            dst_off[k] = db * p.d_sb + dh * p.d_sh + (int64_t)n * p.d_sn + c * 16;
+            x[k] = *(const uint4 *)(p.src + so);
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k)
+            if (dst_off[k] >= 0)
+                *(uint4 *)(p.dst + dst_off[k]) = x[k];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_head_relayout(const RelayoutParams &p, hipStream_t st)
+{
+    const uint64_t total = (uint64_t)p.units * p.F * p.N;
+    if (total == 0)
+        return hipSuccess;
+    uint64_t blocks = (total + 256 * kUnroll - 1) / (256 * kUnroll);
+    if (blocks > 256 * 32)
+        blocks = 256 * 32;
+    hipLaunchKernelGGL(head_relayout_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace seqattn

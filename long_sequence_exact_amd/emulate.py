@@ -11,7 +11,9 @@ block, KV segment) pairs are issued, in which order, with which offset.
   are skipped.
 * DeepSpeed-Ulysses ("DeepSpeed-Ulysses" article, Wie DeepSpeed-Ulysses
   funktioniert: after the all-to-all a GPU sees the whole sequence): one call
-  on the GPU's head subset at full length.
+  on the GPU's head subset at full length; ulysses_pipeline_fwd runs P ranks
+  end to end, with the re-layouts around both all-to-alls and the
+  all-to-alls themselves emulated by the library's head re-layout copy.
 * USP ("Boosting Spec Eagle ...", The Solution: Ulysses and Ring combined):
   a head subset swept over KV blocks like a ring rank, forward and backward.
 * Load-balanced causal ring ("Boosting Spec Eagle ...", The Solution: the
@@ -24,7 +26,7 @@ from __future__ import annotations
 
 import torch
 
-from . import attn_segment_bwd, attn_segment_fwd
+from . import attn_segment_bwd, attn_segment_fwd, head_relayout
 
 
 def ring_order(rank: int, P: int):
@@ -181,6 +183,61 @@ def ulysses_fwd(q, k, v, causal: bool = True, scale=None, out_dtype=None):
     """Ulysses share: the GPU's head subset, full sequence, one call."""
     return attn_segment_fwd(q, k, v, causal_offset=0 if causal else None, scale=scale,
                             out_dtype=out_dtype)
+
+
+def _strided(buf, shape, strides):
+    return buf.as_strided(shape, strides, buf.storage_offset())
+
+
+def ulysses_pipeline_fwd(q, k, v, P: int, causal: bool = True, scale=None):
+    """Ulysses over P emulated ranks on one GPU.
+
+    q: [N, H, d], k, v: [N, Hkv, d] (sequence-major; rank r holds rows
+    [r*N/P, (r+1)*N/P)); H and Hkv divisible by P.  Per rank: pack the shard
+    [Ns, H, d] into the send buffer [P][Ns][H/P][d] (chunk g goes to rank g),
+    all-to-all, attention of head group g over the whole sequence (read in
+    place as [N][H/P][d]), the reverse all-to-all of the output, and the
+    unpack to [Ns, H, d].  Here the P ranks' buffers are stacked on a leading
+    rank axis, so each step is one launch for all ranks.
+    Returns (out [N, H, d] bf16, lse [H, N]).
+    """
+    n, H, d = q.shape
+    Hkv = k.shape[1]
+    if n % P or H % P or Hkv % P:
+        raise ValueError("N, H and Hkv must be divisible by P")
+    ns = n // P
+    dev = q.device
+
+    def to_heads(x):
+        """pack + all-to-all: [N, h, d] -> recv [P(g)][P(r)][Ns][h/P][d]."""
+        h = x.shape[1]
+        hp = h // P
+        send = torch.empty((P, P, ns, hp, d), dtype=x.dtype, device=dev)
+        head_relayout(_strided(x, (P, h, ns, d), (ns * h * d, d, h * d, 1)),
+                      _strided(send, (P * P, hp, ns, d), (ns * hp * d, d, hp * d, 1)))
+        recv = torch.empty((P, P, ns, hp, d), dtype=x.dtype, device=dev)
+        blk = ns * hp * d
+        head_relayout(_strided(send, (P, P, ns * hp, d), (blk, P * blk, d, 1)),
+                      _strided(recv, (P, P, ns * hp, d), (P * blk, blk, d, 1)))
+        # group g's whole sequence, read in place as [g][head][row][d]
+        return _strided(recv, (P, hp, n, d), (n * hp * d, d, hp * d, 1))
+
+    qg, kg, vg = to_heads(q), to_heads(k), to_heads(v)
+    hp = H // P
+    o_heads = torch.empty((P, n, hp, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((P, hp, n), dtype=torch.float32, device=dev)
+    attn_segment_fwd(qg, kg, vg, causal_offset=0 if causal else None, scale=scale,
+                     out=_strided(o_heads, (P, hp, n, d), (n * hp * d, d, hp * d, 1)), lse=lse)
+    # reverse all-to-all: [P(g)][P(r)][Ns][hp][d] -> [P(r)][P(g)][Ns][hp][d]
+    blk = ns * hp * d
+    back = torch.empty((P, P, ns, hp, d), dtype=torch.bfloat16, device=dev)
+    head_relayout(_strided(o_heads, (P, P, ns * hp, d), (blk, P * blk, d, 1)),
+                  _strided(back, (P, P, ns * hp, d), (P * blk, blk, d, 1)))
+    # unpack: [P(r)][P(g)][Ns][hp][d] -> [N, H, d]
+    out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    head_relayout(_strided(back, (P * P, hp, ns, d), (ns * hp * d, d, hp * d, 1)),
+                  _strided(out, (P, H, ns, d), (ns * H * d, d, H * d, 1)))
+    return out, lse.reshape(H, n)
 
 
 def usp_fwd_bwd(q, k, v, d_o, n_blocks: int, q_block: int, causal: bool = True,

@@ -9,6 +9,8 @@ the launch stream, inputs already resident in HBM:
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
   usp_gqa_256k_bf16   forward sweep over 8 KV blocks, then backward sweep
+  ulysses_relayout    a rank's [16384, 32, 128] bf16 shard to its all-to-all send
+                      buffer [8][16384][4][128] and back, in GB/s
   lse_merge           standalone merge of two [32, 16384, 128] partials
                       (fp32 accumulator + bf16 partial), reported in GB/s
 FLOPs are algorithmic (4*d per visible pair forward, 10*d backward); bytes
@@ -24,7 +26,7 @@ import json
 import torch
 
 from . import (attn_segment_bwd, attn_segment_fwd, dilated_attn_bwd, dilated_attn_fwd,
-               emulate, lse_merge)
+               emulate, head_relayout, lse_merge)
 from .synth import WORKLOADS, draw, workload_inputs
 
 PEAK_TFLOPS = 2500.0
@@ -113,6 +115,22 @@ def run(name, reps):
         nbytes = oa.numel() * 4 * 2 + ob.numel() * 2 + la.numel() * 4 * 2 + lb.numel() * 4
         return {"workload": name, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
                 "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_GBS, 3), "bytes": nbytes}
+    if name == "ulysses_relayout":
+        # one rank of Ulysses at 8 ranks x 32 heads, 131072 tokens, d = 128:
+        # its [16384, 32, 128] bf16 shard <-> the [8][16384][4][128] send buffer
+        P, ns, H, d = 8, 16384, 32, 128
+        hp = H // P
+        x = torch.randn((ns, H, d), device=dev).to(torch.bfloat16)
+        buf = torch.empty((P, ns, hp, d), dtype=torch.bfloat16, device=dev)
+        xs = x.as_strided((1, H, ns, d), (0, d, H * d, 1))
+        bs = buf.as_strided((P, hp, ns, d), (ns * hp * d, d, hp * d, 1))
+        ms_p = timed(lambda: head_relayout(xs, bs), reps)
+        ms_u = timed(lambda: head_relayout(bs, xs), reps)
+        nbytes = 2 * x.numel() * 2
+        return {"workload": name, "bytes": nbytes, "pack_ms": round(ms_p, 4),
+                "pack_GB/s": round(nbytes / ms_p / 1e6, 1),
+                "unpack_ms": round(ms_u, 4), "unpack_GB/s": round(nbytes / ms_u / 1e6, 1),
+                "frac_hbm_peak": round(nbytes / max(ms_p, ms_u) / 1e6 / PEAK_GBS, 3)}
     w = WORKLOADS.get(name)
     if name == "ring_16k_bf16":
         q, k, v = (t.to(dev) for t in workload_inputs(w))
@@ -190,7 +208,7 @@ def main():
     ap.add_argument("--workload", nargs="*",
                     default=["ulysses_128k_bf16", "ring_16k_bf16", "ring_16k_bf16_zigzag",
                              "longnet_32k_bf16",
-                             "usp_gqa_256k_bf16", "lse_merge"])
+                             "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge"])
     ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
     for name in args.workload:

@@ -214,3 +214,34 @@ def test_dilated_bwd_validation_errors(L):
     assert call(dv_=T(dv.data, _lib.F32, 1, 2, 256, 64)) == ESHAPE
     assert call(dq_=T(dk.data + 512, _lib.F32, 1, 4, 512, 64)) == EALIAS
     assert call(dv_=T(q.data, _lib.F32, 1, 2, 512, 64)) == EALIAS
+
+
+def test_head_relayout_validation_errors(L):
+    r = ctypes.byref
+    src = T(BASE, _lib.BF16, 1, 8, 256, 128)
+    dst = T(BASE + (1 << 30), _lib.BF16, 4, 2, 256, 128)
+    call = lambda s=src, d_=dst: L.seqattn_head_relayout(r(s), r(d_), None)
+    assert call(d_=T(dst.data, _lib.F32, 4, 2, 256, 128)) == EDTYPE
+    assert call(d_=T(dst.data, _lib.BF16, 3, 2, 256, 128)) == ESHAPE  # b*h differs
+    assert call(d_=T(dst.data, _lib.BF16, 4, 2, 255, 128)) == ESHAPE
+    # 8-byte vectors (rows padded to 16 bytes)
+    odd = T(BASE, _lib.BF16, 1, 8, 256, 4, stride_n=8, stride_h=256 * 8)
+    odd_d = T(dst.data, _lib.BF16, 4, 2, 256, 4, stride_n=8, stride_h=256 * 8,
+              stride_b=2 * 256 * 8)
+    assert call(s=odd, d_=odd_d) == ESHAPE
+    assert call(d_=T(BASE + 4096, _lib.BF16, 4, 2, 256, 128)) == EALIAS
+    same_rows = T(dst.data, _lib.BF16, 4, 2, 256, 128, stride_h=0)
+    assert call(d_=same_rows) == ESTRIDE
+    big_s = T(BASE, _lib.BF16, 1, 1 << 10, 1 << 18, 128)
+    big_d = T(BASE + (1 << 40), _lib.BF16, 1, 1 << 10, 1 << 18, 128)
+    assert call(s=big_s, d_=big_d) == EUNSUP
+    assert call(s=T(BASE, _lib.BF16, 1, 8, 0, 128), d_=T(dst.data, _lib.BF16, 4, 2, 0, 128)) == OK
+
+
+def test_outputs_with_overlapping_rows_are_rejected(L):
+    r = ctypes.byref
+    q, k, v, o, lse = qkvo()
+    o_bad = T(o.data, o.dtype, 1, 4, 256, 128, stride_h=0)
+    assert fwd(L, q, k, v, o_bad, lse) == ESTRIDE
+    lse_bad = _lib.Tensor(lse.data, _lib.F32, 1, 4, 256, 1, 4 * 256, 128, 1)
+    assert fwd(L, q, k, v, o, lse_bad) == ESTRIDE
