@@ -16,6 +16,12 @@ block, KV segment) pairs are issued, in which order, with which offset.
   all-to-alls themselves emulated by the library's head re-layout copy.
 * USP ("Boosting Spec Eagle ...", The Solution: Ulysses and Ring combined):
   a head subset swept over KV blocks like a ring rank, forward and backward.
+* LongNet as a distributed trainer ("LongNet: Scaling Transformers to
+  1,000,000,000 Tokens", LONGNET as a Distributed Trainer): each device holds
+  N/P tokens; a branch whose segments fit in a device is computed locally,
+  a longer one all-gathers the segment's selected keys/values and the local
+  selected queries cross-attend to them; in the backward the all-gather
+  becomes a reduce-scatter (here: accumulation into the owners' rows).
 * Load-balanced causal ring ("Boosting Spec Eagle ...", The Solution: the
   ring's per-step work; the plain causal ring leaves rank r idle for the
   P-1-r steps whose KV block lies in its future).  The sequence is cut into
@@ -26,7 +32,8 @@ from __future__ import annotations
 
 import torch
 
-from . import attn_segment_bwd, attn_segment_fwd, head_relayout
+from . import (attn_segment_bwd, attn_segment_fwd, dilated_attn_bwd, dilated_attn_fwd,
+               head_relayout)
 
 
 def ring_order(rank: int, P: int):
@@ -238,6 +245,139 @@ def ulysses_pipeline_fwd(q, k, v, P: int, causal: bool = True, scale=None):
     head_relayout(_strided(back, (P * P, hp, ns, d), (ns * hp * d, d, hp * d, 1)),
                   _strided(out, (P, H, ns, d), (ns * H * d, d, H * d, 1)))
     return out, lse.reshape(H, n)
+
+
+def _split_branches(n, P, segment_lengths, dilations):
+    """Local (w divides the device share) and gathered (w a multiple of it)
+    branches of LongNet's distributed split."""
+    if n % P:
+        raise ValueError("N must be divisible by the device count")
+    share = n // P
+    local, gathered = [], []
+    for w, r in zip(segment_lengths, dilations):
+        w = min(int(w), n)
+        if share % w == 0:
+            local.append((w, int(r)))
+        elif w % share == 0:
+            gathered.append((w, int(r)))
+        else:
+            raise ValueError(f"segment length {w} neither divides nor is a multiple "
+                             f"of the device share {share}")
+    if not local:
+        raise ValueError("at least one branch must fit in a device share")
+    return share, local, gathered
+
+
+def _gathered_parts(n, P, share, w, r):
+    """For a gathered branch: per segment (start, selected-row count) and per
+    device (segment start, first selected position p0, local selected count,
+    index i0 of p0 among the segment's selected rows)."""
+    segs = []
+    for s0 in range(0, n, w):
+        seglen = min(w, n - s0)
+        segs.append((s0, -(-seglen // r)))
+    devs = []
+    for dev in range(P):
+        a, b = dev * share, (dev + 1) * share
+        s0 = (a // w) * w
+        p0 = s0 + (-(-(a - s0) // r)) * r
+        cnt = -(-(b - p0) // r) if p0 < b else 0
+        devs.append((s0, p0, cnt, (p0 - s0) // r))
+    return segs, devs
+
+
+def _rows(t, start, count, step):
+    """Rows start, start+step, ... (count of them) of a [1,H,N(,d)] tensor."""
+    st = t.stride()
+    off = t.storage_offset() + start * st[2]
+    if t.dim() == 4:
+        return t.as_strided((t.shape[0], t.shape[1], count, t.shape[3]),
+                            (st[0], st[1], step * st[2], st[3]), off)
+    return t.as_strided((t.shape[0], t.shape[1], count), (st[0], st[1], step * st[2]), off)
+
+
+def _all_gather_selected(x, segs, devs, s_start, w, r):
+    """Each device's selected rows of segment s_start, placed at its slot of the
+    gathered [1,H,count,d] buffer (the all-gather's result)."""
+    count = dict(segs)[s_start]
+    g = torch.empty((1, x.shape[1], count, x.shape[3]), dtype=x.dtype, device=x.device)
+    for seg0, p0, cnt, i0 in devs:
+        if seg0 == s_start and cnt > 0:
+            head_relayout(_rows(x, p0, cnt, r), g[:, :, i0:i0 + cnt, :])
+    return g
+
+
+def longnet_split_fwd(q, k, v, segment_lengths, dilations, P: int, causal: bool = False,
+                      scale=None):
+    """Dilated attention with the sequence split over P emulated devices.
+
+    q, k, v: [1,H,N,d] bf16.  Device r holds rows [r*N/P, (r+1)*N/P).  Branches
+    whose segment length divides the share run as dilated attention on the
+    device's rows; for a longer branch, the selected K/V rows of each segment
+    are all-gathered (each device's part copied into its slot) and each
+    device's selected queries attend to them with the causal offset of their
+    place in the segment, merged into the device's running (O, LSE).
+    Returns fp32 O [1,H,N,d] and LSE [1,H,N], equal to dilated_attn_fwd's.
+    """
+    n = q.shape[-2]
+    share, local, gathered = _split_branches(n, P, segment_lengths, dilations)
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    lw, lr = [w for w, _ in local], [r for _, r in local]
+    for dev in range(P):
+        rows = slice(dev * share, (dev + 1) * share)
+        dilated_attn_fwd(q[..., rows, :], k[..., rows, :], v[..., rows, :], lw, lr,
+                         causal=causal, scale=scale, out=out[..., rows, :], lse=lse[..., rows])
+    for w, r in gathered:
+        segs, devs = _gathered_parts(n, P, share, w, r)
+        for s0, _ in segs:
+            kg = _all_gather_selected(k, segs, devs, s0, w, r)
+            vg = _all_gather_selected(v, segs, devs, s0, w, r)
+            for seg0, p0, cnt, i0 in devs:
+                if seg0 != s0 or cnt == 0:
+                    continue
+                attn_segment_fwd(_rows(q, p0, cnt, r), kg, vg,
+                                 causal_offset=i0 if causal else None, scale=scale,
+                                 out=_rows(out, p0, cnt, r), lse=_rows(lse, p0, cnt, r),
+                                 accumulate=True)
+    return out, lse
+
+
+def longnet_split_bwd(q, k, v, out, lse, d_o, segment_lengths, dilations, P: int,
+                      causal: bool = False, scale=None):
+    """Backward of longnet_split_fwd from its merged (out, lse).
+
+    Local branches: the dilated backward on each device's rows.  Gathered
+    branches: each device's selected queries against the gathered K/V; the
+    gradients of the gathered rows are summed over the segment's devices and
+    land on the rows' owners (the reduce-scatter), emulated by accumulating
+    into the global dK/dV rows.  Returns (dq, dk, dv), fp32.
+    """
+    n = q.shape[-2]
+    share, local, gathered = _split_branches(n, P, segment_lengths, dilations)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    lw, lr = [w for w, _ in local], [r for _, r in local]
+    for dev in range(P):
+        rows = slice(dev * share, (dev + 1) * share)
+        dilated_attn_bwd(q[..., rows, :], k[..., rows, :], v[..., rows, :], out[..., rows, :],
+                         lse[..., rows], d_o[..., rows, :], lw, lr, causal=causal, scale=scale,
+                         dq=dq[..., rows, :], dk=dk[..., rows, :], dv=dv[..., rows, :])
+    for w, r in gathered:
+        segs, devs = _gathered_parts(n, P, share, w, r)
+        for s0, count in segs:
+            kg = _all_gather_selected(k, segs, devs, s0, w, r)
+            vg = _all_gather_selected(v, segs, devs, s0, w, r)
+            for seg0, p0, cnt, i0 in devs:
+                if seg0 != s0 or cnt == 0:
+                    continue
+                attn_segment_bwd(_rows(q, p0, cnt, r), kg, vg, _rows(out, p0, cnt, r),
+                                 _rows(lse, p0, cnt, r), _rows(d_o, p0, cnt, r),
+                                 causal_offset=i0 if causal else None, scale=scale,
+                                 dq=_rows(dq, p0, cnt, r), dk=_rows(dk, s0, count, r),
+                                 dv=_rows(dv, s0, count, r), accumulate_kv=True)
+    return dq, dk, dv
 
 
 def usp_fwd_bwd(q, k, v, d_o, n_blocks: int, q_block: int, causal: bool = True,

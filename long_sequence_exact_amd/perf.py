@@ -8,6 +8,8 @@ the launch stream, inputs already resident in HBM:
   ring_16k_bf16_zigzag  the same with the load-balanced zigzag split
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
+  longnet_page_32k_bf16  causal, r = 1,2,4,6,12: single-GPU and split over 4
+                      emulated devices (all-gathered long segments), fwd + bwd
   usp_gqa_256k_bf16   forward sweep over 8 KV blocks, then backward sweep
   ulysses_relayout    a rank's [16384, 32, 128] bf16 shard to its all-to-all send
                       buffer [8][16384][4][128] and back, in GB/s
@@ -44,6 +46,17 @@ def pairs(nq, nk, delta):
         a, b = lo + delta + 1, hi + delta
         tot += (a + b) * (hi - lo) // 2
     tot += max(0, nq - max(lo, hi)) * nk
+    return tot
+
+
+def dilated_pairs(n, segment_lengths, dilations, causal):
+    """Visible (query, key) pairs summed over the branches of dilated attention."""
+    tot = 0
+    for w, r in zip(segment_lengths, dilations):
+        w = min(w, n)
+        for s0 in range(0, n, w):
+            m = -(-min(w, n - s0) // r)
+            tot += m * (m + 1) // 2 if causal else m * m
     return tot
 
 
@@ -158,8 +171,7 @@ def run(name, reps):
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
         ms = timed(lambda: dilated_attn_fwd(q, k, v, w.segment_lengths, w.dilations,
                                             out=out, lse=lse), reps)
-        npairs = sum((w.nq // sl) * (sl // r) ** 2
-                     for sl, r in zip(w.segment_lengths, w.dilations))
+        npairs = dilated_pairs(w.nq, w.segment_lengths, w.dilations, w.causal)
         fl = 4.0 * w.d * w.hq * npairs
         dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
         dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
@@ -171,6 +183,30 @@ def run(name, reps):
                 "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl,
                 "bwd_ms": round(ms_b, 3), "bwd_TFLOP/s": round(fl_b / ms_b / 1e9, 1),
                 "bwd_frac_peak": round(fl_b / ms_b / 1e9 / PEAK_TFLOPS, 3)}
+    elif name == "longnet_page_32k_bf16":
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
+        ws, rs, P = w.segment_lengths, w.dilations, w.segments
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        ms = timed(lambda: dilated_attn_fwd(q, k, v, ws, rs, causal=True, out=out, lse=lse),
+                   reps)
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        ms_b = timed(lambda: dilated_attn_bwd(q, k, v, out, lse, do, ws, rs, causal=True,
+                                              dq=dq, dk=dk, dv=dv), reps)
+        ms_sf = timed(lambda: emulate.longnet_split_fwd(q, k, v, ws, rs, P, causal=True), reps)
+        ms_sb = timed(lambda: emulate.longnet_split_bwd(q, k, v, out, lse, do, ws, rs, P,
+                                                        causal=True), reps)
+        npairs = dilated_pairs(w.nq, ws, rs, True)
+        fl, fl_b = 4.0 * w.d * w.hq * npairs, 10.0 * w.d * w.hq * npairs
+        return {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
+                "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl,
+                "bwd_ms": round(ms_b, 3), "bwd_TFLOP/s": round(fl_b / ms_b / 1e9, 1),
+                "split_devices": P, "split_fwd_ms": round(ms_sf, 3),
+                "split_fwd_TFLOP/s": round(fl / ms_sf / 1e9, 1),
+                "split_bwd_ms": round(ms_sb, 3),
+                "split_bwd_TFLOP/s": round(fl_b / ms_sb / 1e9, 1)}
     elif name == "usp_gqa_256k_bf16":
         q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
         blk = w.nk // w.segments
@@ -207,7 +243,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", nargs="*",
                     default=["ulysses_128k_bf16", "ring_16k_bf16", "ring_16k_bf16_zigzag",
-                             "longnet_32k_bf16",
+                             "longnet_32k_bf16", "longnet_page_32k_bf16",
                              "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge"])
     ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()

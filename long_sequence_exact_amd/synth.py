@@ -80,6 +80,13 @@ WORKLOADS = {
                                  32768, 32768, 64, False, 3,
                                  segment_lengths=(2048, 4096, 8192, 16384, 32768),
                                  dilations=(1, 2, 4, 8, 16)),
+    # LongNet's language-model setting: w = 2048..32768 with r = 1, 2, 4, 6, 12
+    # (r does not divide w for the last two branches), causal; split over
+    # 4 devices of 8192 tokens for the distributed emulation (segments = 4).
+    "longnet_page_32k_bf16": Workload("longnet_page_32k_bf16", torch.bfloat16, 16, 16,
+                                      32768, 32768, 64, True, 5, segments=4,
+                                      segment_lengths=(2048, 4096, 8192, 16384, 32768),
+                                      dilations=(1, 2, 4, 6, 12)),
     # USP share: GQA 8/2 heads, local Q block 7 of 8 (32768 rows) against
     # 8 KV blocks of 32768 (262144 keys), forward + backward.
     "usp_gqa_256k_bf16": Workload("usp_gqa_256k_bf16", torch.bfloat16, 8, 2,

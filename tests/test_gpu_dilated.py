@@ -5,6 +5,7 @@ import torch
 
 import oracle
 import long_sequence_exact_amd as sa
+from long_sequence_exact_amd import emulate
 from long_sequence_exact_amd.synth import WORKLOADS, draw, sample_rows, workload_inputs
 from tests.parity import TOL, assert_parity, dilated_key_list, normwise_per_head, to_np
 
@@ -137,3 +138,72 @@ def test_longnet_32k_bwd_full_size_sampled_and_invariants():
         sdk = dk[0, g].double().sum(0).cpu()
         mag = dk[0, g].double().abs().sum(0).cpu().max()
         assert sdk.abs().max() <= 1e-3 * mag
+
+
+SPLIT_CASES = [
+    # (n, P, hq, hkv, d, ws, rs, causal)
+    (768, 4, 2, 2, 64, (48, 96, 384, 768), (1, 2, 6, 12), True),
+    (768, 4, 4, 2, 128, (48, 96, 384, 768), (1, 2, 6, 12), False),
+    (1152, 3, 2, 1, 64, (128, 384, 768), (1, 4, 6), True),     # tail segment
+]
+
+
+@pytest.mark.parametrize("n,P,hq,hkv,d,ws,rs,causal", SPLIT_CASES)
+def test_longnet_split_matches_oracle_small(n, P, hq, hkv, d, ws, rs, causal):
+    q, k, v, do = draw([(1, hq, n, d), (1, hkv, n, d), (1, hkv, n, d), (1, hq, n, d)],
+                       900 + n + d)
+    o_ref, l_ref = oracle.dilated_fwd(_np32(q), _np32(k), _np32(v), ws, rs, causal=causal)
+    ref = oracle.dilated_bwd(_np32(q), _np32(k), _np32(v), _np32(do), ws, rs, causal=causal)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = emulate.longnet_split_fwd(qd, kd, vd, ws, rs, P, causal=causal)
+    grads = emulate.longnet_split_bwd(qd, kd, vd, o, lse, dod, ws, rs, P, causal=causal)
+    torch.cuda.synchronize()
+    assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="longnet split fwd")
+    _grads_parity(grads, ref, "longnet split bwd")
+
+
+def test_longnet_page_config_full_size_sampled():
+    """LongNet's own mixture (w = 2048..32768, r = 1,2,4,6,12), causal, 16
+    heads, d=64, 32768 tokens: the single-GPU path and the 4-device split,
+    sampled forward rows and dQ rows against the oracle, dK/dV through the
+    sum identities."""
+    w = WORKLOADS["longnet_page_32k_bf16"]
+    ws, rs, P = w.segment_lengths, w.dilations, w.segments
+    q, k, v, do = workload_inputs(w, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o1, l1 = sa.dilated_attn_fwd(qd, kd, vd, ws, rs, causal=True)
+    g1 = sa.dilated_attn_bwd(qd, kd, vd, o1, l1, dod, ws, rs, causal=True)
+    o2, l2 = emulate.longnet_split_fwd(qd, kd, vd, ws, rs, P, causal=True)
+    g2 = emulate.longnet_split_bwd(qd, kd, vd, o2, l2, dod, ws, rs, P, causal=True)
+    torch.cuda.synchronize()
+    rows = []
+    for h in (0, 7, 15):
+        must = (0, 11, 12, 8191, 8196, 16392, 24576, w.nq - 1)
+        for i in sample_rows(w.nq, 16, 6000 + h, must=must):
+            rows.append(h * w.nq + i)
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.dilated_fwd(_np32(q), _np32(k), _np32(v), ws, rs, causal=True,
+                                      rows=rows)
+    q32, k32, v32, do32 = (_np32(t)[0] for t in (q, k, v, do))
+    dq_ref = []
+    for row in rows:
+        h, i = divmod(int(row), w.nq)
+        keys = dilated_key_list(i, w.nq, ws, rs, True)
+        r_, _, _ = oracle.attn_bwd_dq_rows(q32[h:h + 1, i:i + 1], k32[h:h + 1, keys],
+                                           v32[h:h + 1, keys], do32[h:h + 1, i:i + 1])
+        dq_ref.append(r_[0])
+    dq_ref = np.array(dq_ref)
+    do64 = do.double()[0]
+    for what, o, lse, (dq, dk, dv) in (("single GPU", o1, l1, g1), ("split", o2, l2, g2)):
+        og = to_np(o).reshape(-1, w.d)[rows]
+        lg = to_np(lse).reshape(-1)[rows]
+        assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // w.nq,
+                      what=f"longnet page {what}")
+        e = normwise_per_head(to_np(dq).reshape(-1, w.d)[rows], dq_ref, rows // w.nq)
+        assert e <= BTOL, f"{what}: sampled dq error {e:.3e}"
+        for g in range(w.hkv):
+            sdv = dv[0, g].double().sum(0).cpu()
+            sdo = do64[g].sum(0)
+            assert (sdv - sdo).abs().max() <= BTOL * sdo.abs().max(), what
+            sdk = dk[0, g].double().sum(0).cpu()
+            assert sdk.abs().max() <= 1e-3 * dk[0, g].double().abs().sum(0).cpu().max(), what

@@ -102,3 +102,35 @@ def test_bench_refuses_multi_gpu():
     p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert p.returncode == 2 and "one GPU" in p.stdout
+
+
+def test_dilated_pair_count_matches_key_lists():
+    from long_sequence_exact_amd.perf import dilated_pairs
+    from tests.parity import dilated_key_list
+    for n, ws, rs, causal in [(200, (16, 40, 100, 400), (1, 3, 8, 12), True),
+                              (96, (24, 96), (2, 4), False),
+                              (130, (64,), (6,), True)]:
+        brute = sum(len(dilated_key_list(p, n, ws, rs, causal)) for p in range(n))
+        assert dilated_pairs(n, ws, rs, causal) == brute
+
+
+@pytest.mark.parametrize("n,P,w,r", [(32768, 4, 32768, 12), (32768, 4, 16384, 6),
+                                     (1152, 3, 768, 6), (768, 4, 384, 5)])
+def test_longnet_split_gathers_each_selected_row_once(n, P, w, r):
+    """Every device's selected rows of a long segment land in distinct,
+    consecutive slots of that segment's gathered buffer, covering it."""
+    from long_sequence_exact_amd.emulate import _gathered_parts
+    share = n // P
+    segs, devs = _gathered_parts(n, P, share, w, r)
+    for s0, count in segs:
+        selected = [p for p in range(s0, min(s0 + w, n)) if (p - s0) % r == 0]
+        assert len(selected) == count
+        slots = []
+        for dev, (seg0, p0, cnt, i0) in enumerate(devs):
+            if seg0 != s0:
+                continue
+            mine = [p for p in selected if dev * share <= p < (dev + 1) * share]
+            assert mine == list(range(p0, p0 + cnt * r, r))[:len(mine)] and len(mine) == cnt
+            assert selected[i0:i0 + cnt] == mine
+            slots.extend(range(i0, i0 + cnt))
+        assert slots == list(range(count))
