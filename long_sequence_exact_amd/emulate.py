@@ -22,10 +22,11 @@ block, KV segment) pairs are issued, in which order, with which offset.
   a longer one all-gathers the segment's selected keys/values and the local
   selected queries cross-attend to them; in the backward the all-gather
   becomes a reduce-scatter (here: accumulation into the owners' rows).
-* Load-balanced causal ring ("Boosting Spec Eagle ...", The Solution: the
-  ring's per-step work; the plain causal ring leaves rank r idle for the
-  P-1-r steps whose KV block lies in its future).  The sequence is cut into
-  2P chunks and rank r holds chunks r and 2P-1-r, so every step gives every
+* Load-balanced causal ring ("Boosting Spec Eagle ...", Implementation
+  Details and Next Steps: load balancing so that every device of the ring is
+  used effectively; the plain causal ring leaves rank r idle for the P-1-r
+  steps whose KV block lies in its future).  The sequence is cut into 2P
+  chunks and rank r holds chunks r and 2P-1-r, so every step gives every
   rank the same number of visible pairs.
 """
 from __future__ import annotations
