@@ -13,11 +13,13 @@
 //   * one workgroup = 8 waves = 256 query rows of one (batch, segment, head);
 //     each wave owns 32 query rows for the whole kernel; two waves share a
 //     SIMD, so one wave's softmax VALU work overlaps the other's MFMAs;
-//   * the workgroup walks the KV segment in tiles of 128 keys, staged
-//     HBM -> VGPR -> LDS with range-checked buffer loads (rows past the
-//     segment end read as zeros); the next tile's loads are issued before the
-//     current tile is computed; V stays row-major and is read transposed
-//     (ds_read_b64_tr_b16) as the A operand of the PV product;
+//   * the workgroup walks the KV segment in tiles of 128 keys, double-
+//     buffered in LDS and filled by direct HBM -> LDS buffer loads (rows past
+//     the segment end read as zeros), so staging costs no VGPRs and one
+//     barrier per tile orders the fill of tile t+1 after every wave's reads
+//     of tile t-1; rows are unpadded and XOR-swizzled per 16-byte chunk so
+//     the operand reads are bank-conflict free; V stays row-major and is
+//     read transposed (ds_read_b64_tr_b16) as the A operand of the PV product;
 //   * per tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //     (K from LDS as the A operand, Q held in VGPRs as the B operand), so the
 //     accumulator puts one query row in one lane column: the row max needs a
@@ -52,21 +54,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 headroom before the max is raised
+constexpr int kBK = 128;              // keys per K/V tile
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-
-template <int D>
-struct Cfg {
-    static constexpr int BK = 128;                    // keys per tile
-    // LDS row pitches (bf16 elements).  K: +8 so the 32 rows an MFMA operand
-    // read touches fall in distinct banks.  V: a pitch of 16 (mod 64) dwords,
-    // so the four rows x 32 bytes each 16-lane group of a transposing read
-    // touches, and the neighbouring group's, cover all 64 banks once.
-    static constexpr int KSTR = D + 8;
-    static constexpr int VSTR = D + 32;
-    static constexpr int CH = BK * D / 8;             // 16-byte chunks per tile
-    static constexpr int CPT = CH / kThreads;         // chunks per thread (K and V each)
-    static_assert(CPT * kThreads == CH, "tile split");
-};
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -104,13 +93,33 @@ __device__ inline v4i16 read_tr(const bf16 *p)
             (__attribute__((address_space(3))) bf16 *)p)));
 }
 
+// XOR swizzles of the unpadded K and V tiles (16-byte chunk index within a
+// row).  K is read as MFMA operands, 16 lanes = 16 consecutive rows x one
+// chunk per phase: the swizzle must spread those over all 16 bank groups of
+// 16 bytes.  V is read by transposing 8-byte reads, a phase = 4 consecutive
+// rows x 4 chunks (64 bytes each): the swizzle must move each row's 4 chunks
+// to a different bank group of 64 bytes.
+template <int D>
+__device__ inline int kswz(int row)
+{
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);  // 256-byte or 128-byte rows
+}
+template <int D>
+__device__ inline int vswz(int row)
+{
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 {
-    using C = Cfg<D>;
-    constexpr int BK = C::BK;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[BK * C::KSTR];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[BK * C::VSTR];
+    constexpr int BK = kBK;
+    constexpr int ROWB = D * 2;                  // unpadded row of D/8 16-byte chunks
+    constexpr int NCH = D / 8;
+    constexpr int RPP = 1024 / ROWB;             // rows per 1 KiB DMA piece
+    constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
+    constexpr int PPW = TILEB / 1024 / kWaves;   // DMA pieces per wave
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -166,49 +175,49 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     float l_run = 0.f;        // this lane's partial row sum
     const float c = p.scale * kLog2e;
 
-    // staging: thread tid moves 16-byte chunks tid + u*kThreads of the K and
-    // the V tile (row = chunk / (D/8), column = 8 * (chunk % (D/8)))
-    u32x4 kreg[C::CPT], vreg[C::CPT];
-    int srow[C::CPT], scol[C::CPT];
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-        const int ch = tid + u * kThreads;
-        srow[u] = ch / (D / 8);
-        scol[u] = (ch % (D / 8)) * 8;
-    }
-    auto load_tile = [&](int t) {
+    // K/V tiles go HBM -> LDS by direct buffer loads into unpadded rows:
+    // piece u of this wave covers tile rows RPP (wave PPW + u) .. +RPP; lane L
+    // fills LDS chunk L of the piece = row RPP piece + L/NCH, physical chunk
+    // L%NCH, which holds logical chunk (L%NCH) ^ swizzle(row) (kswz, vswz).
+    auto issue_tile = [&](int t) {
         const int j0 = t * BK;
+        char *kb = lds + (t & 1) * 2 * TILEB;
+        char *vb = kb + TILEB;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));  // recompute per tile, keep no offsets live
 #pragma unroll
-        for (int u = 0; u < C::CPT; ++u) {
-            kreg[u] = load16(kr, ((j0 + srow[u]) * (int)p.k.sn + scol[u]) * 2);
-            vreg[u] = load16(vr, ((j0 + srow[u]) * (int)p.v.sn + scol[u]) * 2);
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int u = 0; u < C::CPT; ++u) {
-            *(u32x4 *)(&Ks[srow[u] * C::KSTR + scol[u]]) = kreg[u];
-            *(u32x4 *)(&Vs[srow[u] * C::VSTR + scol[u]]) = vreg[u];
+        for (int u = 0; u < PPW; ++u) {
+            const int piece = wave * PPW + u;
+            const int row = RPP * piece + ln / NCH;
+            const int ph = ln % NCH;
+            const int ko = ((j0 + row) * (int)p.k.sn + ((ph ^ kswz<D>(row)) * 8)) * 2;
+            const int vo = ((j0 + row) * (int)p.v.sn + ((ph ^ vswz<D>(row)) * 8)) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void *)(kb + piece * 1024), 16, ko, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void *)(vb + piece * 1024), 16, vo, 0, 0, 0);
         }
     };
 
-    // transposing-read addresses of the PV A operand (V^T, rows d, k = keys):
-    // read r of k-slice ks, d-block i: lane (group gg = lane/16, i' = lane%16)
-    // addresses V[16ks + 8r + 4(gg/2) + i'/4][32i + 16(gg%2) + 4(i'%4)], so
-    // lane l receives V[16ks + 8r + 4hl + e][32i + l32], e = 0..3 -- the key
-    // order of the P^T accumulator rows.
+    // LDS read offsets: K operand (row 32 kb + l32, logical chunk 2 kk + hl);
+    // V^T operand (row 16 ks + 8 rr + 4 (gg/2) + ip/4, logical chunk
+    // 4 i + 2 (gg%2) + (ip%4)/2, 8-byte half ip%2)
+    const int ksw = kswz<D>(l32);  // rows 32 kb + l32 share l32's swizzle
     const int gg = lane >> 4, ip = lane & 15;
-    const int vt_off = (4 * (gg >> 1) + (ip >> 2)) * C::VSTR + 16 * (gg & 1) + 4 * (ip & 3);
+    const int vrow = 4 * (gg >> 1) + (ip >> 2);  // + 16 ks + 8 rr, same swizzle
+    const int vbase = vrow * ROWB + (2 * (gg & 1) + ((ip & 3) >> 1)) * 16 + (ip & 1) * 8;
+    const int vsw = vswz<D>(vrow) >> 2;
 
     if (ntiles > 0)
-        load_tile(0);
+        issue_tile(0);
 
     for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();  // every wave is done reading the previous tile
-        store_tile();
+        // tile t landed (own loads, then everyone's) and every wave is done
+        // with tile t-1, whose buffer tile t+1 now fills
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 1 < ntiles)
-            load_tile(t + 1);
+            issue_tile(t + 1);
+        const char *kbuf = lds + (t & 1) * 2 * TILEB;
+        const char *vbuf = kbuf + TILEB;
 
         const int j0 = t * BK;
         // whole tile in this wave's causal future: nothing to compute
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
                 sacc[kb][e] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 a = *(const bf16x8 *)(&Ks[(kb * 32 + l32) * C::KSTR + kk * 16 + hl * 8]);
+                const bf16x8 a = *(const bf16x8 *)(kbuf + (kb * 32 + l32) * ROWB + (((2 * kk + hl) ^ ksw) * 16));
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[kb], 0, 0, 0);
             }
         }
@@ -301,9 +310,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const bf16 *base = &Vs[(16 * ks) * C::VSTR + 32 * i + vt_off];
-                const v4i16 lo = read_tr(base);
-                const v4i16 hi = read_tr(base + 8 * C::VSTR);
+                const char *base = vbuf + 16 * ks * ROWB + vbase + ((i ^ vsw) << 6);
+                const v4i16 lo = read_tr((const bf16 *)base);
+                const v4i16 hi = read_tr((const bf16 *)(base + 8 * ROWB));
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
             }
@@ -367,6 +376,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     if (hl == 0)
         *Lp = M + __logf(tot);
 }
+
 
 }  // namespace
 

@@ -192,6 +192,31 @@ def test_zigzag_ring_matches_full_causal_attention_small(P, c, H, d):
     assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="zigzag ring small")
 
 
+@pytest.mark.parametrize("delta", [None, 0, 150])
+def test_growing_scores_take_the_rescale_path(delta):
+    """Keys that line up more and more with the queries: each later block of
+    keys scores far above the running maximum of the earlier ones, so the
+    kernel's reference maximum is raised and the accumulated O rescaled
+    several times per row (random inputs never get there)."""
+    H, N, d = 2, 900, 128
+    g = torch.Generator().manual_seed(31)
+    u = torch.randn(H, 1, d, generator=g)
+    q = (u.expand(H, N, d) + 0.1 * torch.randn(H, N, d, generator=g)).to(torch.bfloat16)
+    a = torch.zeros(N)
+    for j0, amp in ((100, 1.0), (300, 2.5), (500, 4.0), (700, 6.0)):
+        a[j0:] = amp
+    k = (a[None, :, None] * u + torch.randn(H, N, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(H, N, d, generator=g).to(torch.bfloat16)
+    dl = oracle.NONCAUSAL if delta is None else delta
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=dl)
+    o, lse = sa.attn_segment_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal_offset=delta,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    sc = _np32(q)[0] @ _np32(k)[0].T / np.sqrt(d)  # head 0 scores
+    assert sc[:, 700:].max() - sc[:, :100].max() > 40  # far beyond the 2^8 slack
+    assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="growing scores")
+
+
 def _sampled_check(q, k, v, o, lse, delta, rows_per_head, seed, must_rows=(0, -1)):
     """Oracle on a seeded row subset of every head; compare the GPU rows."""
     B, H, N, d = q.shape
