@@ -90,7 +90,8 @@ def _blocks(t, P, blk, first_block, count):
     return _rows_batch(t, first_block * blk, blk, blk, count)
 
 
-def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True):
+def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True,
+             lanes: int = 4):
     """All P ranks of a ring, run one after another on one GPU.
 
     q, k, v: [B,H,N,d]; rank r owns rows [r*N/P, (r+1)*N/P).  Returns the
@@ -100,7 +101,10 @@ def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = T
     r = t..P-1 hold KV block j = r - t, all with the same offset t*N/P, so
     they form one strided batch (ranks r < t hold j = r - t + P, which is in
     the causal future and skipped, or one more batch when non-causal).
-    batched=False issues one launch per (rank, step).
+    With lanes > 1 the ranks are split by r % lanes, each class running its
+    steps as such batches on a stream of its own: the classes' launches
+    overlap, so one launch's epilogues (the fused merges) run while another
+    computes.  batched=False issues one launch per (rank, step).
     """
     B, H, n, d = q.shape
     blk = n // P
@@ -112,16 +116,32 @@ def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = T
             sweep_fwd(q[..., rows, :], k, v, P, r, causal, out[..., rows, :], lse[..., rows],
                       scale=scale)
         return out, lse
-    for t in range(P):
-        groups = [(t, P - t, 0)]                 # (first rank, ranks, first KV block)
-        if not causal and t > 0:
-            groups.append((0, t, P - t))
-        for r0, cnt, j0 in groups:
-            delta = (r0 - j0) * blk if causal else None
-            attn_segment_fwd(_blocks(q, P, blk, r0, cnt), _blocks(k, P, blk, j0, cnt),
-                             _blocks(v, P, blk, j0, cnt), causal_offset=delta, scale=scale,
-                             out=_blocks(out, P, blk, r0, cnt), lse=_blocks(lse, P, blk, r0, cnt),
-                             accumulate=t > 0)
+    lanes = max(1, min(lanes, P))
+    main = torch.cuda.current_stream(q.device)
+    streams = [main] if lanes == 1 else [torch.cuda.Stream(q.device) for _ in range(lanes)]
+    for st in streams[1:] if lanes == 1 else streams:
+        st.wait_stream(main)
+    for lane, st in enumerate(streams):
+        with torch.cuda.stream(st):
+            for t in range(P):
+                groups = [(t, P - t, 0)]             # (first rank, ranks, first KV block)
+                if not causal and t > 0:
+                    groups.append((0, t, P - t))
+                for g0, gcnt, j0 in groups:
+                    # this lane's ranks of the group: g0 + i, i = lane' ... step lanes
+                    r0 = g0 + (lane - g0) % lanes
+                    cnt = len(range(r0, g0 + gcnt, lanes))
+                    if cnt == 0:
+                        continue
+                    jr = j0 + (r0 - g0)
+                    delta = (r0 - jr) * blk if causal else None
+                    rb = lambda x, first: _rows_batch(x, first * blk, blk, lanes * blk, cnt)
+                    attn_segment_fwd(rb(q, r0), rb(k, jr), rb(v, jr), causal_offset=delta,
+                                     scale=scale, out=rb(out, r0), lse=rb(lse, r0),
+                                     accumulate=t > 0)
+    if lanes > 1:
+        for st in streams:
+            main.wait_stream(st)
     return out, lse
 
 

@@ -4,7 +4,8 @@
 
 For each synthetic workload the whole hot path is timed with HIP events on
 the launch stream, inputs already resident in HBM:
-  ring_16k_bf16       8 ranks x 8 KV segments, fused-merge ring sweep
+  ring_16k_bf16       8 ranks x 8 KV segments, fused-merge ring sweep (ranks split
+                      over 4 streams; also timed on one stream)
   ring_16k_bf16_zigzag  the same with the load-balanced zigzag split
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
@@ -148,6 +149,7 @@ def run(name, reps):
     if name == "ring_16k_bf16":
         q, k, v = (t.to(dev) for t in workload_inputs(w))
         ms = timed(lambda: emulate.ring_fwd(q, k, v, w.segments, causal=True), reps)
+        ms1 = timed(lambda: emulate.ring_fwd(q, k, v, w.segments, causal=True, lanes=1), reps)
         fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
         crit, busy = ring_critical_path(q, k, v, w.segments, False, reps)
     elif name == "ring_16k_bf16_zigzag":
@@ -231,6 +233,10 @@ def run(name, reps):
         raise ValueError(name)
     res = {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
            "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl}
+    if name == "ring_16k_bf16":
+        # `ms`: 4 rank classes on 4 streams (the driver's default); one stream:
+        res.update({"one_stream_ms": round(ms1, 3),
+                    "one_stream_TFLOP/s": round(fl / ms1 / 1e9, 1)})
     if name.startswith("ring_16k"):
         # one device per rank: per-step slowest rank, summed over the steps
         res.update({"rank_critical_path_ms": round(crit, 3),

@@ -217,6 +217,18 @@ def test_growing_scores_take_the_rescale_path(delta):
     assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="growing scores")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_lanes_give_identical_results(causal):
+    """Splitting the ranks over streams keeps every rank's merge order, so the
+    result is bit-identical to the one-stream sweep."""
+    q, k, v = (t.to(DEV) for t in draw([(1, 4, 1024, 128)] * 3, 3))
+    o1, l1 = emulate.ring_fwd(q, k, v, 8, causal=causal, lanes=1)
+    for lanes in (2, 3, 4, 8):
+        o, l = emulate.ring_fwd(q, k, v, 8, causal=causal, lanes=lanes)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1) and torch.equal(l, l1), lanes
+
+
 def _sampled_check(q, k, v, o, lse, delta, rows_per_head, seed, must_rows=(0, -1)):
     """Oracle on a seeded row subset of every head; compare the GPU rows."""
     B, H, N, d = q.shape
