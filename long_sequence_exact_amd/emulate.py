@@ -84,6 +84,14 @@ def _rows_batch(t, row0, rows, step, count):
     return t.as_strided((count, t.shape[1], rows), (step * st[2], st[1], st[2]), off)
 
 
+def lane_entries(first_rank: int, count: int, lane: int, lanes: int):
+    """Entries of a rank batch (ranks first_rank .. first_rank + count - 1)
+    that belong to stream lane `lane` of `lanes` (rank % lanes == lane):
+    (index of the first such entry, how many; they are `lanes` apart)."""
+    b0 = (lane - first_rank) % lanes
+    return b0, len(range(b0, count, lanes))
+
+
 def _blocks(t, P, blk, first_block, count):
     """View of `count` consecutive length-blk row blocks of t starting at
     block `first_block`, as a batch: [count, H, blk(, d)]."""
@@ -91,7 +99,7 @@ def _blocks(t, P, blk, first_block, count):
 
 
 def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True,
-             lanes: int = 4):
+             lanes: int = 2):
     """All P ranks of a ring, run one after another on one GPU.
 
     q, k, v: [B,H,N,d]; rank r owns rows [r*N/P, (r+1)*N/P).  Returns the
@@ -128,11 +136,10 @@ def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = T
                 if not causal and t > 0:
                     groups.append((0, t, P - t))
                 for g0, gcnt, j0 in groups:
-                    # this lane's ranks of the group: g0 + i, i = lane' ... step lanes
-                    r0 = g0 + (lane - g0) % lanes
-                    cnt = len(range(r0, g0 + gcnt, lanes))
+                    b0, cnt = lane_entries(g0, gcnt, lane, lanes)
                     if cnt == 0:
                         continue
+                    r0 = g0 + b0
                     jr = j0 + (r0 - g0)
                     delta = (r0 - jr) * blk if causal else None
                     rb = lambda x, first: _rows_batch(x, first * blk, blk, lanes * blk, cnt)
@@ -183,12 +190,14 @@ def zigzag_plan(n: int, P: int):
     return plan
 
 
-def zigzag_ring_fwd(q, k, v, P: int, scale=None, out=None, lse=None):
+def zigzag_ring_fwd(q, k, v, P: int, scale=None, out=None, lse=None, lanes: int = 4):
     """Causal ring over P ranks with the zigzag split, all ranks on one GPU.
 
     q, k, v: [1,H,N,d] in the zigzag layout (zigzag_order; rank r owns rows
     [r*2c, (r+1)*2c)).  Returns the merged fp32 output and LSE in the same
-    layout.  Issues the launches of zigzag_plan.
+    layout.  Issues the launches of zigzag_plan; with lanes > 1 the ranks of
+    each launch are split by r % lanes over as many streams, so every rank's
+    steps stay in order on one stream while the classes overlap.
     """
     _, H, n, d = q.shape
     if q.shape[0] != 1:
@@ -199,11 +208,26 @@ def zigzag_ring_fwd(q, k, v, P: int, scale=None, out=None, lse=None):
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    for _, (q0, qn, cnt), (k0, kn, _), delta, acc in plan:
-        attn_segment_fwd(_rows_batch(q, q0, qn, step, cnt), _rows_batch(k, k0, kn, step, cnt),
-                         _rows_batch(v, k0, kn, step, cnt), causal_offset=delta, scale=scale,
-                         out=_rows_batch(out, q0, qn, step, cnt),
-                         lse=_rows_batch(lse, q0, qn, step, cnt), accumulate=acc)
+    lanes = max(1, min(lanes, P))
+    main = torch.cuda.current_stream(q.device)
+    streams = [main] if lanes == 1 else [torch.cuda.Stream(q.device) for _ in range(lanes)]
+    if lanes > 1:
+        for st in streams:
+            st.wait_stream(main)
+    for lane, st in enumerate(streams):
+        with torch.cuda.stream(st):
+            for _, (q0, qn, cnt), (k0, kn, _), delta, acc in plan:
+                b0, m = lane_entries(q0 // step, cnt, lane, lanes)  # q0 // step: first rank
+                if m == 0:
+                    continue
+                qs, ks = q0 + b0 * step, k0 + b0 * step
+                rb = lambda x, first, rows: _rows_batch(x, first, rows, lanes * step, m)
+                attn_segment_fwd(rb(q, qs, qn), rb(k, ks, kn), rb(v, ks, kn), causal_offset=delta,
+                                 scale=scale, out=rb(out, qs, qn), lse=rb(lse, qs, qn),
+                                 accumulate=acc)
+    if lanes > 1:
+        for st in streams:
+            main.wait_stream(st)
     return out, lse
 
 

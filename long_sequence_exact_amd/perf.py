@@ -5,7 +5,7 @@
 For each synthetic workload the whole hot path is timed with HIP events on
 the launch stream, inputs already resident in HBM:
   ring_16k_bf16       8 ranks x 8 KV segments, fused-merge ring sweep (ranks split
-                      over 4 streams; also timed on one stream)
+                      over 2 streams; also timed on one stream)
   ring_16k_bf16_zigzag  the same with the load-balanced zigzag split
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
@@ -59,6 +59,18 @@ def dilated_pairs(n, segment_lengths, dilations, causal):
             m = -(-min(w, n - s0) // r)
             tot += m * (m + 1) // 2 if causal else m * m
     return tot
+
+
+def warm_up(seconds=1.0):
+    """Run the forward kernel untimed for about `seconds`, so the first timed
+    workload does not run at ramping clocks."""
+    import time
+    q, k, v = (t.to("cuda") for t in draw([(1, 4, 16384, 128)] * 3, 99))
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            attn_segment_fwd(q, k, v, causal_offset=0)
+        torch.cuda.synchronize()
 
 
 def timed(fn, reps, warmup=2):
@@ -159,6 +171,8 @@ def run(name, reps):
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
         ms = timed(lambda: emulate.zigzag_ring_fwd(q, k, v, w.segments, out=out, lse=lse), reps)
+        ms1 = timed(lambda: emulate.zigzag_ring_fwd(q, k, v, w.segments, out=out, lse=lse,
+                                                    lanes=1), reps)
         fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
         crit, busy = ring_critical_path(q, k, v, w.segments, True, reps)
     elif name == "ulysses_128k_bf16":
@@ -233,8 +247,8 @@ def run(name, reps):
         raise ValueError(name)
     res = {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
            "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl}
-    if name == "ring_16k_bf16":
-        # `ms`: 4 rank classes on 4 streams (the driver's default); one stream:
+    if name.startswith("ring_16k"):
+        # `ms`: rank classes on streams (the drivers' default lanes); one stream:
         res.update({"one_stream_ms": round(ms1, 3),
                     "one_stream_TFLOP/s": round(fl / ms1 / 1e9, 1)})
     if name.startswith("ring_16k"):
@@ -253,6 +267,7 @@ def main():
                              "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge"])
     ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
+    warm_up()
     for name in args.workload:
         print(json.dumps(run(name, args.reps)), flush=True)
 

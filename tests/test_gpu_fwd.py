@@ -227,6 +227,14 @@ def test_ring_lanes_give_identical_results(causal):
         o, l = emulate.ring_fwd(q, k, v, 8, causal=causal, lanes=lanes)
         torch.cuda.synchronize()
         assert torch.equal(o, o1) and torch.equal(l, l1), lanes
+    if causal:
+        order = torch.tensor(emulate.zigzag_order(1024, 8), device=DEV)
+        qz, kz, vz = (t[:, :, order].contiguous() for t in (q, k, v))
+        z1 = emulate.zigzag_ring_fwd(qz, kz, vz, 8, lanes=1)
+        for lanes in (2, 4, 8):
+            z = emulate.zigzag_ring_fwd(qz, kz, vz, 8, lanes=lanes)
+            torch.cuda.synchronize()
+            assert torch.equal(z[0], z1[0]) and torch.equal(z[1], z1[1]), lanes
 
 
 def _sampled_check(q, k, v, o, lse, delta, rows_per_head, seed, must_rows=(0, -1)):

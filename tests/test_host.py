@@ -7,7 +7,7 @@ import torch
 from bench import visible_pairs
 import numpy as np
 
-from long_sequence_exact_amd.emulate import ring_order, zigzag_order, zigzag_plan
+from long_sequence_exact_amd.emulate import lane_entries, ring_order, zigzag_order, zigzag_plan
 from long_sequence_exact_amd.synth import WORKLOADS, draw, sample_rows
 
 
@@ -134,3 +134,17 @@ def test_longnet_split_gathers_each_selected_row_once(n, P, w, r):
             assert selected[i0:i0 + cnt] == mine
             slots.extend(range(i0, i0 + cnt))
         assert slots == list(range(count))
+
+
+@pytest.mark.parametrize("lanes", [1, 2, 3, 4, 8])
+def test_stream_lanes_partition_every_rank_batch(lanes):
+    """Each launch's rank batch is split over the stream lanes by rank % lanes:
+    every entry exactly once, and a rank always on the same lane."""
+    for first, count in [(0, 8), (3, 5), (7, 1), (0, 1), (2, 6)]:
+        seen = []
+        for lane in range(lanes):
+            b0, m = lane_entries(first, count, lane, lanes)
+            entries = [b0 + i * lanes for i in range(m)]
+            assert all((first + b) % lanes == lane for b in entries)
+            seen += entries
+        assert sorted(seen) == list(range(count))
