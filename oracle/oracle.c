@@ -193,20 +193,39 @@ void oracle_lse_merge(const double *oa, const double *la, const double *ob,
 /* Dilated attention                                                         */
 /* ------------------------------------------------------------------------- */
 
+/* Key list of query p in a branch (segment length w, dilation r, offset s
+ * inside the segment; causal keeps keys at original positions <= p).
+ * Returns the count, or -1 if the branch does not select p. */
+static int64_t dilated_keys(int64_t p, int64_t N, int64_t w, int64_t r,
+                            int64_t s, int32_t causal, int64_t *keys)
+{
+    const int64_t seg0 = (p / w) * w;
+    if (p - seg0 < s || (p - seg0 - s) % r != 0)
+        return -1;
+    int64_t n = 0;
+    for (int64_t t = seg0 + s; t < seg0 + w && t < N; t += r)
+        if (!causal || t <= p)
+            keys[n++] = t;
+    return n;
+}
+
 /*
  * oracle_dilated_fwd: for each branch b (segment length w[b], dilation
- * r[b]) a position p is selected iff (p mod w[b]) mod r[b] == 0; a selected
- * query p attends to the selected keys of its segment floor(p / w[b]) (and,
- * when causal != 0, only to keys at original positions <= p).  Each branch
- * gives a partial (O_b, LSE_b) -- (0, -inf) for an unselected p -- and the
- * partials are folded with the log-sum-exp merge in branch order.
+ * r[b]) a position p is selected iff (p mod w[b]) - s is a non-negative
+ * multiple of r[b], where the offset s is 0, or h mod r[b] for query head h
+ * when head_shift != 0 (LongNet's multi-head variant: heads spread over the
+ * r[b] residue classes).  A selected query p attends to the keys of its
+ * segment floor(p / w[b]) at the same offsets (and, when causal != 0, only
+ * to keys at original positions <= p).  Each branch gives a partial
+ * (O_b, LSE_b) -- (0, -inf) for an unselected p -- and the partials are
+ * folded with the log-sum-exp merge in branch order.
  * q, k, v share the length N.  rows as in oracle_attn_fwd.
  */
 void oracle_dilated_fwd(const float *q, const float *k, const float *v,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                         int64_t d, const int64_t *w, const int64_t *r,
-                        int32_t nb, int32_t causal, double scale,
-                        const int64_t *rows, int64_t nrows,
+                        int32_t nb, int32_t causal, int32_t head_shift,
+                        double scale, const int64_t *rows, int64_t nrows,
                         double *o_out, double *lse_out)
 {
     const double sigma = pick_scale(scale, d);
@@ -236,13 +255,10 @@ void oracle_dilated_fwd(const float *q, const float *k, const float *v,
             for (int64_t c = 0; c < d; ++c)
                 acc[c] = 0.0;
             for (int32_t b = 0; b < nb; ++b) {
-                if ((p % w[b]) % r[b] != 0)
+                const int64_t off = head_shift ? h % r[b] : 0;
+                const int64_t n = dilated_keys(p, N, w[b], r[b], off, causal, keys);
+                if (n < 0)
                     continue; /* (0, -inf): the merge identity */
-                const int64_t seg0 = (p / w[b]) * w[b];
-                int64_t n = 0;
-                for (int64_t t = seg0; t < seg0 + w[b] && t < N; t += r[b])
-                    if (!causal || t <= p)
-                        keys[n++] = t;
                 row_attention(q + flat * d, kb, vb, keys, n, d, sigma, s, ob,
                               &lb);
                 merge_row(acc, lacc, ob, lb, d, tmp, &lnew);
@@ -433,22 +449,6 @@ int oracle_num_threads(void)
 /* Dilated attention backward                                                */
 /* ------------------------------------------------------------------------- */
 
-/* Key list of query p in branch b (segment-relative dilation; causal keeps
- * keys at original positions <= p).  Returns the count; 0 if p is not
- * selected by the branch. */
-static int64_t dilated_keys(int64_t p, int64_t N, int64_t w, int64_t r,
-                            int32_t causal, int64_t *keys)
-{
-    if ((p % w) % r != 0)
-        return 0;
-    const int64_t seg0 = (p / w) * w;
-    int64_t n = 0;
-    for (int64_t t = seg0; t < seg0 + w && t < N; t += r)
-        if (!causal || t <= p)
-            keys[n++] = t;
-    return n;
-}
-
 /*
  * oracle_dilated_bwd: gradients of L = sum(dO * O) for the dilated attention
  * of oracle_dilated_fwd.  Folding branch partials with the log-sum-exp merge
@@ -461,8 +461,9 @@ static int64_t dilated_keys(int64_t p, int64_t N, int64_t w, int64_t r,
 void oracle_dilated_bwd(const float *q, const float *k, const float *v,
                         const float *dout, int64_t B, int64_t Hq, int64_t Hkv,
                         int64_t N, int64_t d, const int64_t *w, const int64_t *r,
-                        int32_t nb, int32_t causal, double scale,
-                        double *dq_out, double *dk_out, double *dv_out)
+                        int32_t nb, int32_t causal, int32_t head_shift,
+                        double scale, double *dq_out, double *dk_out,
+                        double *dv_out)
 {
     const double sigma = pick_scale(scale, d);
     const int64_t nq_rows = B * Hq * N;
@@ -475,8 +476,8 @@ void oracle_dilated_bwd(const float *q, const float *k, const float *v,
             wmax = w[b];
 
     /* global O, LSE (the forward definition) and D per query row */
-    oracle_dilated_fwd(q, k, v, B, Hq, Hkv, N, d, w, r, nb, causal, scale, NULL,
-                       nq_rows, o, lse);
+    oracle_dilated_fwd(q, k, v, B, Hq, Hkv, N, d, w, r, nb, causal, head_shift,
+                       scale, NULL, nq_rows, o, lse);
 #pragma omp parallel for schedule(static)
     for (int64_t row = 0; row < nq_rows; ++row) {
         double acc = 0.0;
@@ -499,7 +500,8 @@ void oracle_dilated_bwd(const float *q, const float *k, const float *v,
             for (int64_t c = 0; c < d; ++c)
                 dq[c] = 0.0;
             for (int32_t b = 0; b < nb; ++b) {
-                const int64_t n = dilated_keys(p, N, w[b], r[b], causal, keys);
+                const int64_t off = head_shift ? h % r[b] : 0;
+                const int64_t n = dilated_keys(p, N, w[b], r[b], off, causal, keys);
                 for (int64_t t = 0; t < n; ++t) {
                     const float *krow = k + ((bt * Hkv + g) * N + keys[t]) * d;
                     const float *vrow = v + ((bt * Hkv + g) * N + keys[t]) * d;
@@ -536,8 +538,9 @@ void oracle_dilated_bwd(const float *q, const float *k, const float *v,
                     continue;
                 for (int32_t b = 0; b < nb; ++b) {
                     const int64_t seg0 = (j / w[b]) * w[b];
+                    const int64_t off = head_shift ? h % r[b] : 0;
                     for (int64_t p = seg0; p < seg0 + w[b] && p < N; ++p) {
-                        const int64_t n = dilated_keys(p, N, w[b], r[b], causal, keys);
+                        const int64_t n = dilated_keys(p, N, w[b], r[b], off, causal, keys);
                         int listed = 0;
                         for (int64_t t = 0; t < n; ++t)
                             if (keys[t] == j)

@@ -49,13 +49,13 @@ def _load():
     D = ctypes.c_double
     lib.oracle_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, D, P, I, P, P]
     lib.oracle_lse_merge.argtypes = [P, P, P, P, I, I, P, P]
-    lib.oracle_dilated_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P,
+    lib.oracle_dilated_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, D, P, I, P, P]
     lib.oracle_attn_bwd_dq_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D,
                                             P, I, P, P, P]
     lib.oracle_attn_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P, P]
     lib.oracle_dilated_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, P, ctypes.c_int32,
-                                       ctypes.c_int32, D, P, P, P]
+                                       ctypes.c_int32, ctypes.c_int32, D, P, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     for f in ("oracle_attn_fwd", "oracle_lse_merge", "oracle_dilated_fwd",
               "oracle_attn_bwd_dq_rows", "oracle_attn_bwd", "oracle_dilated_bwd"):
@@ -135,8 +135,10 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
 
 
 def dilated_fwd(q, k, v, segment_lengths, dilations, causal=False, scale=0.0,
-                rows=None):
-    """LongNet dilated attention, branch partials folded by the LSE merge."""
+                rows=None, head_shift=False):
+    """LongNet dilated attention, branch partials folded by the LSE merge.
+    head_shift: query head h selects offset h mod r_i inside each segment
+    (offset 0 for every head otherwise)."""
     lib = _load()
     q4, k4, v4 = _as4(q), _as4(k), _as4(v)
     B, Hq, N, d = q4.shape
@@ -150,7 +152,8 @@ def dilated_fwd(q, k, v, segment_lengths, dilations, causal=False, scale=0.0,
     lse = np.empty((n,), np.float64)
     lib.oracle_dilated_fwd(_ptr(q4), _ptr(k4), _ptr(v4), B, Hq, Hkv, N, d,
                            _ptr(w), _ptr(rr), len(w), int(bool(causal)),
-                           float(scale), _ptr(r), n, _ptr(o), _ptr(lse))
+                           int(bool(head_shift)), float(scale), _ptr(r), n, _ptr(o),
+                           _ptr(lse))
     if r is None:
         o = o.reshape(B, Hq, N, d)
         lse = lse.reshape(B, Hq, N)
@@ -193,7 +196,8 @@ def attn_bwd(q, k, v, dout, delta=NONCAUSAL, scale=0.0):
     return dq, dk, dv
 
 
-def dilated_bwd(q, k, v, dout, segment_lengths, dilations, causal=False, scale=0.0):
+def dilated_bwd(q, k, v, dout, segment_lengths, dilations, causal=False, scale=0.0,
+                head_shift=False):
     """(dQ, dK, dV) of L = sum(dO * O) for dilated_fwd's attention."""
     lib = _load()
     q4, k4, v4, do4 = _as4(q), _as4(k), _as4(v), _as4(dout)
@@ -205,8 +209,8 @@ def dilated_bwd(q, k, v, dout, segment_lengths, dilations, causal=False, scale=0
     dk = np.empty((B, Hkv, N, d), np.float64)
     dv = np.empty((B, Hkv, N, d), np.float64)
     lib.oracle_dilated_bwd(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(do4), B, Hq, Hkv, N, d,
-                           _ptr(w), _ptr(rr), len(w), int(bool(causal)), float(scale),
-                           _ptr(dq), _ptr(dk), _ptr(dv))
+                           _ptr(w), _ptr(rr), len(w), int(bool(causal)),
+                           int(bool(head_shift)), float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
     if np.asarray(q).ndim == 3:
         return dq[0], dk[0], dv[0]
     return dq, dk, dv

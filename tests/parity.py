@@ -63,18 +63,20 @@ def assert_parity(o, lse, o_ref, lse_ref, dtype, rows_heads=None, what=""):
     return e, le
 
 
-def dilated_key_list(p, n, ws, rs, causal):
+def dilated_key_list(p, n, ws, rs, causal, shift=0):
     """Keys that the dilated branches (w_i, r_i) list for query p, a key once
     per listing branch: branch i selects p when p's offset in its w_i-segment
-    is a multiple of r_i, and then lists the selected positions of that
-    segment (with causal, those <= p)."""
+    is shift mod r_i plus a multiple of r_i, and then lists the selected
+    positions of that segment (with causal, those <= p).  shift is the query
+    head under head-dependent offsets, else 0."""
     keys = []
     for w, r in zip(ws, rs):
         w = min(w, n)
         s0 = (p // w) * w
-        if (p - s0) % r:
+        off = shift % r
+        if p - s0 < off or (p - s0 - off) % r:
             continue
-        ks = np.arange(s0, min(s0 + w, n), r)
+        ks = np.arange(s0 + off, min(s0 + w, n), r)
         if causal:
             ks = ks[ks <= p]
         keys.append(ks)

@@ -362,13 +362,15 @@ def test_dilated_r1_short_segments_is_block_diagonal():
     assert np.abs(o - _sdpa(q, k, v, mask=blk)).max() < 1e-12
 
 
-def _multiplicity(n, ws, rs, causal):
+def _multiplicity(n, ws, rs, causal, shift=0):
     """c[p, j]: how many branches let query p attend key j (segment-relative
-    dilation: offset inside the length-w segment a multiple of r)."""
+    dilation: offset inside the length-w segment equal to shift mod r plus a
+    multiple of r)."""
     c = np.zeros((n, n))
     pos = np.arange(n)
     for w, r in zip(ws, rs):
-        sel = (pos % w) % r == 0
+        off = pos % w - shift % r
+        sel = (off >= 0) & (off % r == 0)
         same = (pos[:, None] // w) == (pos[None, :] // w)
         m = same & sel[:, None] & sel[None, :]
         if causal:
@@ -424,6 +426,54 @@ def test_dilated_page_branch_lists_fixture():
     assert np.abs(o - _sdpa(q, k, v, mask=bias)).max() < 1e-12
 
 
+@pytest.mark.parametrize("ws,rs,causal,group", [
+    ((8, 16, 32, 64), (1, 2, 4, 8), False, 1),
+    ((12, 40, 64), (1, 3, 6), True, 1),      # tails; offsets past a tail's end
+    ((16, 64), (2, 4), False, 2),            # no dense branch; GQA
+])
+def test_dilated_head_shift_equals_per_head_multiset_union(ws, rs, causal, group):
+    # With head-dependent offsets, query head h of branch (w, r) selects the
+    # positions at offset h mod r (plus multiples of r) inside each segment;
+    # per head this is again one softmax over a multiset union, built here
+    # from positions alone and checked with a library attention.
+    n, d, hq = 64, 8, 8 * group
+    q = _rand((1, hq, n, d), 350)
+    k = _rand((1, 8, n, d), 351)
+    v = _rand((1, 8, n, d), 352)
+    o, lse = oracle.dilated_fwd(q, k, v, ws, rs, causal=causal, head_shift=True)
+    o0, _ = oracle.dilated_fwd(q, k, v, ws, rs, causal=causal)
+    assert np.abs(o - o0).max() > 1e-3          # the option changes the function
+    for h in range(hq):
+        c = _multiplicity(n, ws, rs, causal, shift=h)
+        live = c.sum(1) > 0
+        with np.errstate(divide="ignore"):
+            bias = np.log(c)
+        g = h // group
+        ref = _sdpa(q[:, h:h + 1, live], k[:, g:g + 1], v[:, g:g + 1], mask=bias[live])
+        assert np.abs(o[:, h:h + 1, live] - ref).max() < 1e-12, h
+        assert np.all(o[:, h, ~live] == 0) and np.all(np.isneginf(lse[:, h, ~live]))
+
+
+def test_dilated_head_shift_single_branch_is_strided_attention():
+    # One branch (w = N, r = H): head h attends among positions h, h + r, ...
+    # only, so it is plain attention on that strided subsequence, and across
+    # heads every position is selected exactly once.
+    n, d, r = 60, 8, 4
+    q = _rand((1, r, n, d), 360)
+    k = _rand((1, r, n, d), 361)
+    v = _rand((1, r, n, d), 362)
+    o, lse = oracle.dilated_fwd(q, k, v, [n], [r], head_shift=True)
+    covered = np.zeros(n, int)
+    for h in range(r):
+        sub = slice(h, n, r)
+        ref = _sdpa(q[:, h:h + 1, sub], k[:, h:h + 1, sub], v[:, h:h + 1, sub])
+        assert np.abs(o[:, h:h + 1, sub] - ref).max() < 1e-12
+        live = np.isfinite(lse[0, h])
+        assert np.array_equal(np.flatnonzero(live), np.arange(h, n, r))
+        covered += live
+    assert np.all(covered == 1)
+
+
 def test_dilated_row_subset():
     n, d = 64, 8
     q = _rand((1, 2, n, d), 340)
@@ -468,6 +518,37 @@ def test_dilated_bwd_matches_library_autograd(ws, rs, causal, group):
     assert np.abs(dk - kt.grad.numpy()).max() < 1e-12
     assert np.abs(dv - vt.grad.numpy()).max() < 1e-12
     assert np.all(dq[:, :, ~live] == 0)
+
+
+@pytest.mark.parametrize("ws,rs,causal,group", [
+    ((8, 16, 32), (1, 2, 4), True, 1),
+    ((12, 24), (2, 6), False, 2),          # GQA: a KV head serves two offsets
+])
+def test_dilated_bwd_head_shift_matches_library_autograd(ws, rs, causal, group):
+    n, d, hq = 32, 8, 4 * group
+    q = _rand((1, hq, n, d), 440)
+    k = _rand((1, 4, n, d), 441)
+    v = _rand((1, 4, n, d), 442)
+    do = _rand((1, hq, n, d), 443)
+    dq, dk, dv = oracle.dilated_bwd(q, k, v, do, ws, rs, causal=causal, head_shift=True)
+    qt = torch.from_numpy(q.astype(np.float64)).requires_grad_()
+    kt = torch.from_numpy(k.astype(np.float64)).requires_grad_()
+    vt = torch.from_numpy(v.astype(np.float64)).requires_grad_()
+    dot = torch.from_numpy(do.astype(np.float64))
+    loss = 0
+    for h in range(hq):
+        c = _multiplicity(n, ws, rs, causal, shift=h)
+        live = c.sum(1) > 0
+        with np.errstate(divide="ignore"):
+            bias = torch.from_numpy(np.log(c[live]))
+        g = h // group
+        o = F.scaled_dot_product_attention(qt[:, h:h + 1, live], kt[:, g:g + 1],
+                                           vt[:, g:g + 1], attn_mask=bias)
+        loss = loss + (o * dot[:, h:h + 1, live]).sum()
+    loss.backward()
+    assert np.abs(dq - qt.grad.numpy()).max() < 1e-12
+    assert np.abs(dk - kt.grad.numpy()).max() < 1e-12
+    assert np.abs(dv - vt.grad.numpy()).max() < 1e-12
 
 
 def test_dilated_bwd_finite_differences():

@@ -31,8 +31,10 @@ MUTANTS = {
                               "dq[c] += sigma * ds * (double)vrow[c];"),
     "dv_uses_ds": ("dv[c] += p * (double)dorow[c];",
                    "dv[c] += ds * (double)dorow[c];"),
-    "dilation_not_segment_relative": ("if ((p % w[b]) % r[b] != 0)",
-                                      "if (p % r[b] != 0)"),
+    "dilation_not_segment_relative": ("(p - seg0 - s) % r != 0", "(p - s) % r != 0"),
+    "head_shift_keys_unshifted": ("for (int64_t t = seg0 + s;", "for (int64_t t = seg0;"),
+    "head_shift_by_kv_head": ("const int64_t off = head_shift ? h % r[b] : 0;",
+                              "const int64_t off = head_shift ? g % r[b] : 0;"),
     "dilated_causal_strict": ("if (!causal || t <= p)", "if (!causal || t < p)"),
     "dilated_merge_drops_branch": ("merge_row(acc, lacc, ob, lb, d, tmp, &lnew);",
                                    "merge_row(ob, lb, ob, lb, d, tmp, &lnew);"),
