@@ -80,6 +80,8 @@ typedef struct {
                                  the new partial is merged into them */
 #define SEQATTN_CAUSAL 2u     /* dilated attention only: causal in original
                                  positions */
+#define SEQATTN_HEAD_SHIFT 4u /* dilated attention only: query head h selects
+                                 offset h mod r_i inside each segment */
 
 /* op ids for seqattn_workspace_size */
 #define SEQATTN_OP_SEGMENT_FWD 0
@@ -149,7 +151,12 @@ int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
  * is a multiple of r_i; selected queries attend to the selected keys of the
  * same segment (SEQATTN_CAUSAL: only keys at original positions <= the
  * query's); unselected positions get the empty partial; the branch partials
- * are merged by log-sum-exp.
+ * are merged by log-sum-exp.  With SEQATTN_HEAD_SHIFT the offset is h mod
+ * r_i for query head h instead of 0 (positions at offset s, s + r_i, ...;
+ * its keys use the same offset), so the heads of a branch together cover
+ * more positions; LongNet's multi-head variant, which the page's stripped
+ * formulas do not show.  Its cost is one launch per residue class of heads
+ * (multi-head attention) or per query head (grouped KV heads).
  *
  * q: [B, Hq, N, d] bf16; k, v: [B, Hkv, N, d] bf16; o: [B, Hq, N, d] fp32
  * or bf16; lse: [B, Hq, N, 1] fp32.  segment_lengths[i] >= 1 and
@@ -214,7 +221,8 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
  * segment backward above, and the gradients of all branches add up.
  * q, d_o: [B, Hq, N, d] bf16; k, v: [B, Hkv, N, d] bf16; o: [B, Hq, N, d]
  * bf16 or fp32 and lse: [B, Hq, N, 1] fp32, both from the forward with the
- * same (segment_lengths, dilations, flags).  flags: SEQATTN_CAUSAL or 0.
+ * same (segment_lengths, dilations, flags).  flags: SEQATTN_CAUSAL and/or
+ * SEQATTN_HEAD_SHIFT, as in the forward.
  * dq: fp32, ACCUMULATED; dk, dv: [B, Hkv, N, d] fp32, OVERWRITTEN (rows no
  * branch selects get 0).
  * workspace: seqattn_workspace_size(SEQATTN_OP_DILATED_BWD) bytes.

@@ -18,7 +18,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import ACCUMULATE, CAUSAL, NONCAUSAL, SeqattnError
+from ._lib import ACCUMULATE, CAUSAL, HEAD_SHIFT, NONCAUSAL, SeqattnError
 
 __all__ = ["attn_segment_fwd", "lse_merge", "dilated_attn_fwd", "attn_segment_bwd",
            "dilated_attn_bwd", "head_relayout", "workspace_size", "NONCAUSAL", "SeqattnError", "version"]
@@ -75,9 +75,18 @@ def workspace_size(op: int, q, other) -> int:
     return int(L.seqattn_workspace_size(op, ctypes.byref(a), ctypes.byref(b), 0))
 
 
+def _dilated_flags(causal, head_shift):
+    return (CAUSAL if causal else 0) | (HEAD_SHIFT if head_shift else 0)
+
+
 def dilated_attn_fwd(q, k, v, segment_lengths, dilations, causal=False, scale=None,
-                     out=None, lse=None, out_dtype=torch.float32, workspace=None):
-    """LongNet dilated attention: branch partials merged by log-sum-exp."""
+                     out=None, lse=None, out_dtype=torch.float32, workspace=None,
+                     head_shift=False):
+    """LongNet dilated attention: branch partials merged by log-sum-exp.
+
+    head_shift=True: query head h selects offset h mod r_i inside each
+    segment (offset 0 for every head otherwise).
+    """
     L = _lib.lib()
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
@@ -98,7 +107,8 @@ def dilated_attn_fwd(q, k, v, segment_lengths, dilations, causal=False, scale=No
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(L.seqattn_dilated_attn_fwd(
         ctypes.byref(dqd), ctypes.byref(dkd), ctypes.byref(dvd), w, r, n,
-        float(scale or 0.0), CAUSAL if causal else 0, ctypes.byref(dod), ctypes.byref(dld),
+        float(scale or 0.0), _dilated_flags(causal, head_shift), ctypes.byref(dod),
+        ctypes.byref(dld),
         ctypes.c_void_p(wptr), wbytes, ctypes.c_void_p(_lib.stream_handle())))
     return out, lse
 
@@ -138,7 +148,8 @@ def attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, scale=None, dq=No
 
 
 def dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, causal=False,
-                     scale=None, dq=None, dk=None, dv=None, workspace=None):
+                     scale=None, dq=None, dk=None, dv=None, workspace=None,
+                     head_shift=False):
     """Gradients of dilated_attn_fwd from its merged (o, lse).
 
     dq (fp32) is accumulated into (zeros if not given); dk, dv (fp32) are written.
@@ -167,7 +178,8 @@ def dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, causal=Fa
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(L.seqattn_dilated_attn_bwd(
         *[ctypes.byref(x) for x in ds], ctypes.byref(dl), ctypes.byref(ddo), w, r, n,
-        float(scale or 0.0), CAUSAL if causal else 0, ctypes.byref(gq), ctypes.byref(gk),
+        float(scale or 0.0), _dilated_flags(causal, head_shift), ctypes.byref(gq),
+        ctypes.byref(gk),
         ctypes.byref(gv), ctypes.c_void_p(wptr), wbytes,
         ctypes.c_void_p(_lib.stream_handle())))
     return dq, dk, dv

@@ -19,6 +19,7 @@ BF16, F32 = 1, 2
 NONCAUSAL = (1 << 63) - 1
 ACCUMULATE = 1
 CAUSAL = 2
+HEAD_SHIFT = 4
 OP_SEGMENT_FWD, OP_LSE_MERGE, OP_DILATED_FWD, OP_SEGMENT_BWD, OP_DILATED_BWD = 0, 1, 2, 3, 4
 
 EXPORTS = ("seqattn_attn_segment_fwd", "seqattn_lse_merge", "seqattn_dilated_attn_fwd",

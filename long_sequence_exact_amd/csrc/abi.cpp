@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "../../include/seqattn.h"
 #include "common.h"
@@ -221,6 +222,37 @@ int check_head_extent(const seqattn_tensor *t, const char *name, int64_t row_ste
     return SEQATTN_OK;
 }
 
+// The heads one launch of a dilated branch covers and their offset inside
+// the segment.  Without head-dependent offsets (or with r = 1) it is every
+// head at offset 0.  With them, query head h uses offset h mod r: for
+// multi-head attention one launch per residue class c takes heads c, c + r,
+// ... (a head stride of r heads, KV heads alike); with grouped KV heads the
+// query heads of one class do not share a KV-head pattern, so each query
+// head gets a launch of its own with its KV head.
+struct HeadSel {
+    int64_t qh, kh;   // first query head, first KV head
+    int64_t step;     // head stride, in heads
+    int nq, nk;       // query heads, KV heads
+    int64_t off;      // offset inside the segment
+};
+
+std::vector<HeadSel> head_sels(bool shift, int64_t r, int Hq, int Hkv)
+{
+    std::vector<HeadSel> out;
+    if (!shift || r == 1) {
+        out.push_back({0, 0, 1, Hq, Hkv, 0});
+    } else if (Hq == Hkv) {
+        for (int64_t c = 0; c < std::min<int64_t>(r, Hq); ++c) {
+            const int n = (int)((Hq - c + r - 1) / r);
+            out.push_back({c, c, r, n, n, c});
+        }
+    } else {
+        for (int64_t h = 0; h < Hq; ++h)
+            out.push_back({h, (h * Hkv) / Hq, 1, 1, 1, h % r});
+    }
+    return out;
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,7 +400,7 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
         return fail(SEQATTN_ERR_NULL, "segment_lengths / dilations are NULL");
     if (n_branches < 1 || n_branches > 64)
         return fail(SEQATTN_ERR_SHAPE, "n_branches must be in [1, 64]");
-    if (flags & ~SEQATTN_CAUSAL)
+    if (flags & ~(SEQATTN_CAUSAL | SEQATTN_HEAD_SHIFT))
         return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
     for (int i = 0; i < n_branches; ++i)
         if (segment_lengths[i] < 1 || dilations[i] < 1 || segment_lengths[i] >= kMaxRows ||
@@ -413,33 +445,37 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
         if (e != hipSuccess)
             return hip_status(e, "dilated init");
     }
+    const bool shift = flags & SEQATTN_HEAD_SHIFT;
     for (int i = 0; i < n_branches; ++i) {
         const int64_t w = std::min<int64_t>(segment_lengths[i], N), r = dilations[i];
         const int64_t nfull = N / w, tail = N % w;
+        for (const HeadSel &hs : head_sels(shift, r, Hq, (int)k->h))
         for (int part = 0; part < 2; ++part) {
             const int64_t nseg = part == 0 ? nfull : (tail > 0 ? 1 : 0);
             const int64_t seglen = part == 0 ? w : tail;
-            if (nseg == 0)
+            if (nseg == 0 || seglen <= hs.off)
                 continue;
-            const int64_t base = part == 0 ? 0 : nfull * w;   // first row of the part
-            const int64_t rows = (seglen + r - 1) / r;        // selected rows per segment
-            auto sub = [&](View vv, int64_t es, int64_t sn) {
+            const int64_t base = (part == 0 ? 0 : nfull * w) + hs.off;  // first selected row
+            const int64_t rows = (seglen - hs.off + r - 1) / r;        // selected rows per segment
+            // [B][segment][head][selected row] view of the heads hs covers
+            auto sub = [&](View vv, int64_t es, int64_t head0) {
                 View x = vv;
-                x.ptr = (const char *)vv.ptr + base * sn * es;
-                x.ss = w * sn;
-                x.sn = r * sn;
+                x.ptr = (const char *)vv.ptr + (base * vv.sn + head0 * vv.sh) * es;
+                x.sh = hs.step * vv.sh;
+                x.ss = w * vv.sn;
+                x.sn = r * vv.sn;
                 return x;
             };
             FwdParams p;
-            p.q = sub(view_of(q), 2, q->stride_n);
-            p.k = sub(view_of(k), 2, k->stride_n);
-            p.v = sub(view_of(v), 2, v->stride_n);
-            p.o = sub(acc, 4, acc.sn);
-            p.lse = sub(lsev, 4, lse->stride_n);
+            p.q = sub(view_of(q), 2, hs.qh);
+            p.k = sub(view_of(k), 2, hs.kh);
+            p.v = sub(view_of(v), 2, hs.kh);
+            p.o = sub(acc, 4, hs.qh);
+            p.lse = sub(lsev, 4, hs.qh);
             p.B = B;
             p.S = (int)nseg;
-            p.Hq = Hq;
-            p.Hkv = (int)k->h;
+            p.Hq = hs.nq;
+            p.Hkv = hs.nk;
             p.Nq = p.Nk = (int)rows;
             clamp_delta(causal ? 0 : SEQATTN_NONCAUSAL, rows, rows, &p.delta, &p.noncausal);
             p.scale = scale;
@@ -574,7 +610,7 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         return fail(SEQATTN_ERR_NULL, "segment_lengths / dilations are NULL");
     if (n_branches < 1 || n_branches > 64)
         return fail(SEQATTN_ERR_SHAPE, "n_branches must be in [1, 64]");
-    if (flags & ~SEQATTN_CAUSAL)
+    if (flags & ~(SEQATTN_CAUSAL | SEQATTN_HEAD_SHIFT))
         return fail(SEQATTN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
     for (int i = 0; i < n_branches; ++i)
         if (segment_lengths[i] < 1 || dilations[i] < 1 || segment_lengths[i] >= kMaxRows ||
@@ -659,34 +695,40 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
             (e = launch_zero_f32(base.dv, B, Hkv, N, d, s)) != hipSuccess)
             return hip_status(e, "dilated bwd init");
     }
+    const bool shift = flags & SEQATTN_HEAD_SHIFT;
     for (int i = 0; i < n_branches; ++i) {
         const int64_t w = std::min<int64_t>(segment_lengths[i], N), r = dilations[i];
         const int64_t nfull = N / w, tail = N % w;
+        for (const HeadSel &hs : head_sels(shift, r, Hq, Hkv))
         for (int part = 0; part < 2; ++part) {
             const int64_t nseg = part == 0 ? nfull : (tail > 0 ? 1 : 0);
             const int64_t seglen = part == 0 ? w : tail;
-            if (nseg == 0)
+            if (nseg == 0 || seglen <= hs.off)
                 continue;
-            const int64_t row0 = part == 0 ? 0 : nfull * w;
-            const int64_t rows = (seglen + r - 1) / r;
-            // Branch i's selected rows of each segment, as a [B][seg][H][rows] view.
-            auto sub = [&](View vv, int64_t es) {
+            const int64_t row0 = (part == 0 ? 0 : nfull * w) + hs.off;
+            const int64_t rows = (seglen - hs.off + r - 1) / r;
+            // Branch i's selected rows of each segment for the heads hs
+            // covers, as a [B][seg][H][rows] view.
+            auto sub = [&](View vv, int64_t es, int64_t head0) {
                 View x = vv;
-                x.ptr = (const char *)vv.ptr + row0 * vv.sn * es;
+                x.ptr = (const char *)vv.ptr + (row0 * vv.sn + head0 * vv.sh) * es;
+                x.sh = hs.step * vv.sh;
                 x.ss = w * vv.sn;
                 x.sn = r * vv.sn;
                 return x;
             };
             BwdParams p = base;
-            p.q = sub(base.q, 2);
-            p.k = sub(base.k, 2);
-            p.v = sub(base.v, 2);
-            p.lse = sub(base.lse, 4);
-            p.dout = sub(base.dout, 2);
-            p.dq = sub(base.dq, 4);
-            p.dk = sub(base.dk, 4);
-            p.dv = sub(base.dv, 4);
-            p.dvec = sub(base.dvec, 4);
+            p.q = sub(base.q, 2, hs.qh);
+            p.k = sub(base.k, 2, hs.kh);
+            p.v = sub(base.v, 2, hs.kh);
+            p.lse = sub(base.lse, 4, hs.qh);
+            p.dout = sub(base.dout, 2, hs.qh);
+            p.dq = sub(base.dq, 4, hs.qh);
+            p.dk = sub(base.dk, 4, hs.kh);
+            p.dv = sub(base.dv, 4, hs.kh);
+            p.dvec = sub(base.dvec, 4, hs.qh);
+            p.Hq = hs.nq;
+            p.Hkv = hs.nk;
             p.S = (int)nseg;
             p.Nq = p.Nk = (int)rows;
             clamp_delta(causal ? 0 : SEQATTN_NONCAUSAL, rows, rows, &p.delta, &p.noncausal);

@@ -10,7 +10,8 @@ the launch stream, inputs already resident in HBM:
   ulysses_128k_bf16   one causal forward launch (the benchmark's step)
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
   longnet_page_32k_bf16  causal, r = 1,2,4,6,12: single-GPU and split over 4
-                      emulated devices (all-gathered long segments), fwd + bwd
+                      emulated devices (all-gathered long segments), fwd + bwd;
+                      also with head-dependent offsets
   usp_gqa_256k_bf16   forward sweep over 8 KV blocks, then backward sweep
   ulysses_relayout    a rank's [16384, 32, 128] bf16 shard to its all-to-all send
                       buffer [8][16384][4][128] and back, in GB/s
@@ -50,13 +51,15 @@ def pairs(nq, nk, delta):
     return tot
 
 
-def dilated_pairs(n, segment_lengths, dilations, causal):
-    """Visible (query, key) pairs summed over the branches of dilated attention."""
+def dilated_pairs(n, segment_lengths, dilations, causal, shift=0):
+    """Visible (query, key) pairs summed over the branches of dilated attention
+    (one head; shift: the query head under head-dependent offsets)."""
     tot = 0
     for w, r in zip(segment_lengths, dilations):
         w = min(w, n)
+        off = shift % r
         for s0 in range(0, n, w):
-            m = -(-min(w, n - s0) // r)
+            m = max(0, -(-(min(w, n - s0) - off) // r))
             tot += m * (m + 1) // 2 if causal else m * m
     return tot
 
@@ -214,6 +217,13 @@ def run(name, reps):
         ms_sf = timed(lambda: emulate.longnet_split_fwd(q, k, v, ws, rs, P, causal=True), reps)
         ms_sb = timed(lambda: emulate.longnet_split_bwd(q, k, v, out, lse, do, ws, rs, P,
                                                         causal=True), reps)
+        # head-dependent offsets: one launch per residue class of heads
+        ms_hf = timed(lambda: dilated_attn_fwd(q, k, v, ws, rs, causal=True, out=out, lse=lse,
+                                               head_shift=True), reps)
+        ms_hb = timed(lambda: dilated_attn_bwd(q, k, v, out, lse, do, ws, rs, causal=True,
+                                               dq=dq, dk=dk, dv=dv, head_shift=True), reps)
+        hpairs = sum(dilated_pairs(w.nq, ws, rs, True, shift=h) for h in range(w.hq))
+        fl_h, fl_hb = 4.0 * w.d * hpairs, 10.0 * w.d * hpairs
         npairs = dilated_pairs(w.nq, ws, rs, True)
         fl, fl_b = 4.0 * w.d * w.hq * npairs, 10.0 * w.d * w.hq * npairs
         return {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
@@ -222,7 +232,11 @@ def run(name, reps):
                 "split_devices": P, "split_fwd_ms": round(ms_sf, 3),
                 "split_fwd_TFLOP/s": round(fl / ms_sf / 1e9, 1),
                 "split_bwd_ms": round(ms_sb, 3),
-                "split_bwd_TFLOP/s": round(fl_b / ms_sb / 1e9, 1)}
+                "split_bwd_TFLOP/s": round(fl_b / ms_sb / 1e9, 1),
+                "head_shift_fwd_ms": round(ms_hf, 3),
+                "head_shift_fwd_TFLOP/s": round(fl_h / ms_hf / 1e9, 1),
+                "head_shift_bwd_ms": round(ms_hb, 3),
+                "head_shift_bwd_TFLOP/s": round(fl_hb / ms_hb / 1e9, 1)}
     elif name == "usp_gqa_256k_bf16":
         q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
         blk = w.nk // w.segments

@@ -143,6 +143,7 @@ def test_dilated_validation_errors(L):
     w0 = (ctypes.c_int64 * 2)(0, 512)
     assert call(w0, rr, 2) == ESHAPE
     assert call(w, rr, 2, flags=1) == EUNSUP
+    assert call(w, rr, 2, flags=8) == EUNSUP
     assert call(w, rr, 2) == EWS  # bf16 o needs the fp32 workspace
     need = L.seqattn_workspace_size(_lib.OP_DILATED_FWD, r(q), r(o), 2)
     assert need == 2 * 512 * 64 * 4
@@ -205,7 +206,8 @@ def test_dilated_bwd_validation_errors(L):
     assert call(w_=None) == ENULL
     assert call(w_=(ctypes.c_int64 * 2)(128, 0)) == ESHAPE
     assert call(r_=(ctypes.c_int64 * 2)(0, 2)) == ESHAPE
-    assert call(flags=1) == EUNSUP  # only SEQATTN_CAUSAL
+    assert call(flags=1) == EUNSUP  # only SEQATTN_CAUSAL | SEQATTN_HEAD_SHIFT
+    assert call(flags=8) == EUNSUP
     assert call(wsb=need - 4) == EWS
     assert call(ws_=None, wsb=0) == EWS
     assert call(ws_=ws + 4) == EWS  # misaligned

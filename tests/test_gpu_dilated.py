@@ -49,6 +49,34 @@ def test_dilated_small(n, d, hq, hkv, ws, rs, causal):
     assert_parity(to_np(ob), to_np(lb), o_ref, l_ref, torch.bfloat16, what="dilated bf16 out")
 
 
+HEAD_SHIFT_CASES = [
+    # query head h selects offset h mod r inside each segment
+    (512, 64, 8, 8, (64, 128, 256, 512), (1, 2, 4, 8), False),   # heads > r
+    (515, 128, 8, 8, (64, 256, 512), (1, 4, 8), True),           # 3-row tails: offsets past them
+    (640, 64, 6, 6, (80, 160, 320, 640), (1, 2, 6, 12), True),   # r not 2^k, r > heads
+    (384, 64, 4, 2, (96, 384), (2, 4), False),                   # grouped KV heads, first r > 1
+]
+
+
+@pytest.mark.parametrize("n,d,hq,hkv,ws,rs,causal", HEAD_SHIFT_CASES)
+def test_dilated_head_shift_small(n, d, hq, hkv, ws, rs, causal):
+    q, k, v, do = draw([(1, hq, n, d), (1, hkv, n, d), (1, hkv, n, d), (1, hq, n, d)],
+                       560 + n + d)
+    q32, k32, v32, do32 = (_np32(t) for t in (q, k, v, do))
+    o_ref, l_ref = oracle.dilated_fwd(q32, k32, v32, ws, rs, causal=causal, head_shift=True)
+    ref = oracle.dilated_bwd(q32, k32, v32, do32, ws, rs, causal=causal, head_shift=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = sa.dilated_attn_fwd(qd, kd, vd, ws, rs, causal=causal, head_shift=True)
+    ob, lb = sa.dilated_attn_fwd(qd, kd, vd, ws, rs, causal=causal, head_shift=True,
+                                 out_dtype=torch.bfloat16)
+    grads = sa.dilated_attn_bwd(qd, kd, vd, o, lse, dod, ws, rs, causal=causal,
+                                head_shift=True)
+    torch.cuda.synchronize()
+    assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="head shift f32 out")
+    assert_parity(to_np(ob), to_np(lb), o_ref, l_ref, torch.bfloat16, what="head shift bf16 out")
+    _grads_parity(grads, ref, "head shift bwd")
+
+
 def test_longnet_32k_full_size_sampled():
     """16 heads, d=64, 32768 tokens, w = 2048..32768, r = 1..16, non-causal."""
     w = WORKLOADS["longnet_32k_bf16"]
@@ -207,3 +235,47 @@ def test_longnet_page_config_full_size_sampled():
             assert (sdv - sdo).abs().max() <= BTOL * sdo.abs().max(), what
             sdk = dk[0, g].double().sum(0).cpu()
             assert sdk.abs().max() <= 1e-3 * dk[0, g].double().abs().sum(0).cpu().max(), what
+
+
+def test_longnet_page_config_head_shift_full_size_sampled():
+    """LongNet's mixture (w = 2048..32768, r = 1,2,4,6,12), causal, 16 heads,
+    d=64, 32768 tokens, with head h at offset h mod r_i: sampled forward rows
+    and dQ rows against the oracle, dK/dV through the sum identities (the
+    r = 1 branch selects every query)."""
+    w = WORKLOADS["longnet_page_32k_bf16"]
+    ws, rs = w.segment_lengths, w.dilations
+    q, k, v, do = workload_inputs(w, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = sa.dilated_attn_fwd(qd, kd, vd, ws, rs, causal=True, head_shift=True)
+    dq, dk, dv = sa.dilated_attn_bwd(qd, kd, vd, o, lse, dod, ws, rs, causal=True,
+                                     head_shift=True)
+    torch.cuda.synchronize()
+    rows = []
+    for h in (0, 5, 11, 15):
+        must = (0, 5, 11, 12, 2048 + h % 12, 8191, 16392 + h % 4, w.nq - 1)
+        for i in sample_rows(w.nq, 12, 6100 + h, must=must):
+            rows.append(h * w.nq + i)
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.dilated_fwd(_np32(q), _np32(k), _np32(v), ws, rs, causal=True,
+                                      rows=rows, head_shift=True)
+    og = to_np(o).reshape(-1, w.d)[rows]
+    lg = to_np(lse).reshape(-1)[rows]
+    assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // w.nq,
+                  what="longnet page head shift")
+    q32, k32, v32, do32 = (_np32(t)[0] for t in (q, k, v, do))
+    dq_ref = []
+    for row in rows:
+        h, i = divmod(int(row), w.nq)
+        keys = dilated_key_list(i, w.nq, ws, rs, True, shift=h)
+        r_, _, _ = oracle.attn_bwd_dq_rows(q32[h:h + 1, i:i + 1], k32[h:h + 1, keys],
+                                           v32[h:h + 1, keys], do32[h:h + 1, i:i + 1])
+        dq_ref.append(r_[0])
+    e = normwise_per_head(to_np(dq).reshape(-1, w.d)[rows], np.array(dq_ref), rows // w.nq)
+    assert e <= BTOL, f"head shift: sampled dq error {e:.3e}"
+    do64 = do.double()[0]
+    for g in range(w.hkv):
+        sdv = dv[0, g].double().sum(0).cpu()
+        sdo = do64[g].sum(0)
+        assert (sdv - sdo).abs().max() <= BTOL * sdo.abs().max()
+        sdk = dk[0, g].double().sum(0).cpu()
+        assert sdk.abs().max() <= 1e-3 * dk[0, g].double().abs().sum(0).cpu().max()

@@ -110,8 +110,9 @@ def test_dilated_pair_count_matches_key_lists():
     for n, ws, rs, causal in [(200, (16, 40, 100, 400), (1, 3, 8, 12), True),
                               (96, (24, 96), (2, 4), False),
                               (130, (64,), (6,), True)]:
-        brute = sum(len(dilated_key_list(p, n, ws, rs, causal)) for p in range(n))
-        assert dilated_pairs(n, ws, rs, causal) == brute
+        for shift in (0, 1, 5, 11):     # head-dependent offsets
+            brute = sum(len(dilated_key_list(p, n, ws, rs, causal, shift)) for p in range(n))
+            assert dilated_pairs(n, ws, rs, causal, shift) == brute
 
 
 @pytest.mark.parametrize("n,P,w,r", [(32768, 4, 32768, 12), (32768, 4, 16384, 6),
