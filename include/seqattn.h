@@ -155,8 +155,8 @@ int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
  * r_i for query head h instead of 0 (positions at offset s, s + r_i, ...;
  * its keys use the same offset), so the heads of a branch together cover
  * more positions; LongNet's multi-head variant, which the page's stripped
- * formulas do not show.  Its cost is one launch per residue class of heads
- * (multi-head attention) or per query head (grouped KV heads).
+ * formulas do not show.  The kernels apply the offset per head; only the
+ * backward with grouped KV heads takes one launch per query head.
  *
  * q: [B, Hq, N, d] bf16; k, v: [B, Hkv, N, d] bf16; o: [B, Hq, N, d] fp32
  * or bf16; lse: [B, Hq, N, 1] fp32.  segment_lengths[i] >= 1 and

@@ -224,31 +224,28 @@ int check_head_extent(const seqattn_tensor *t, const char *name, int64_t row_ste
 
 // The heads one launch of a dilated branch covers and their offset inside
 // the segment.  Without head-dependent offsets (or with r = 1) it is every
-// head at offset 0.  With them, query head h uses offset h mod r: for
-// multi-head attention one launch per residue class c takes heads c, c + r,
-// ... (a head stride of r heads, KV heads alike); with grouped KV heads the
-// query heads of one class do not share a KV-head pattern, so each query
-// head gets a launch of its own with its KV head.
+// head at offset 0.  With them, query head h uses offset h mod r: the
+// kernels apply it per head themselves (in_kernel), except in the backward
+// with grouped KV heads, whose dK/dV workgroup serves query heads of
+// different offsets; there each query head gets a launch of its own with
+// its KV head.
 struct HeadSel {
     int64_t qh, kh;   // first query head, first KV head
-    int64_t step;     // head stride, in heads
     int nq, nk;       // query heads, KV heads
-    int64_t off;      // offset inside the segment
+    int64_t off;      // offset inside the segment (host-applied)
+    bool in_kernel;   // the kernels shift head h by h mod r
 };
 
-std::vector<HeadSel> head_sels(bool shift, int64_t r, int Hq, int Hkv)
+std::vector<HeadSel> head_sels(bool shift, int64_t r, int Hq, int Hkv, bool kernel_ok)
 {
     std::vector<HeadSel> out;
     if (!shift || r == 1) {
-        out.push_back({0, 0, 1, Hq, Hkv, 0});
-    } else if (Hq == Hkv) {
-        for (int64_t c = 0; c < std::min<int64_t>(r, Hq); ++c) {
-            const int n = (int)((Hq - c + r - 1) / r);
-            out.push_back({c, c, r, n, n, c});
-        }
+        out.push_back({0, 0, Hq, Hkv, 0, false});
+    } else if (kernel_ok) {
+        out.push_back({0, 0, Hq, Hkv, 0, true});
     } else {
         for (int64_t h = 0; h < Hq; ++h)
-            out.push_back({h, (h * Hkv) / Hq, 1, 1, 1, h % r});
+            out.push_back({h, (h * Hkv) / Hq, 1, 1, h % r, false});
     }
     return out;
 }
@@ -449,7 +446,7 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
     for (int i = 0; i < n_branches; ++i) {
         const int64_t w = std::min<int64_t>(segment_lengths[i], N), r = dilations[i];
         const int64_t nfull = N / w, tail = N % w;
-        for (const HeadSel &hs : head_sels(shift, r, Hq, (int)k->h))
+        for (const HeadSel &hs : head_sels(shift, r, Hq, (int)k->h, true))
         for (int part = 0; part < 2; ++part) {
             const int64_t nseg = part == 0 ? nfull : (tail > 0 ? 1 : 0);
             const int64_t seglen = part == 0 ? w : tail;
@@ -461,7 +458,6 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
             auto sub = [&](View vv, int64_t es, int64_t head0) {
                 View x = vv;
                 x.ptr = (const char *)vv.ptr + (base * vv.sn + head0 * vv.sh) * es;
-                x.sh = hs.step * vv.sh;
                 x.ss = w * vv.sn;
                 x.sn = r * vv.sn;
                 return x;
@@ -481,6 +477,8 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
             p.scale = scale;
             p.accumulate = (i == 0 && first_writes) ? 0 : 1;
             p.o_f32 = 1;
+            p.hs_r = hs.in_kernel ? (int)r : 0;
+            p.hs_len = (int)seglen;
             hipError_t e = launch_fwd_bf16(p, d, s);
             if (e != hipSuccess)
                 return hip_status(e, "dilated branch launch");
@@ -699,7 +697,7 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
     for (int i = 0; i < n_branches; ++i) {
         const int64_t w = std::min<int64_t>(segment_lengths[i], N), r = dilations[i];
         const int64_t nfull = N / w, tail = N % w;
-        for (const HeadSel &hs : head_sels(shift, r, Hq, Hkv))
+        for (const HeadSel &hs : head_sels(shift, r, Hq, Hkv, Hq == Hkv))
         for (int part = 0; part < 2; ++part) {
             const int64_t nseg = part == 0 ? nfull : (tail > 0 ? 1 : 0);
             const int64_t seglen = part == 0 ? w : tail;
@@ -712,7 +710,6 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
             auto sub = [&](View vv, int64_t es, int64_t head0) {
                 View x = vv;
                 x.ptr = (const char *)vv.ptr + (row0 * vv.sn + head0 * vv.sh) * es;
-                x.sh = hs.step * vv.sh;
                 x.ss = w * vv.sn;
                 x.sn = r * vv.sn;
                 return x;
@@ -733,6 +730,8 @@ int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
             p.Nq = p.Nk = (int)rows;
             clamp_delta(causal ? 0 : SEQATTN_NONCAUSAL, rows, rows, &p.delta, &p.noncausal);
             p.acc_kv = (i == 0 && first_writes) ? 0 : 1;
+            p.hs_r = hs.in_kernel ? (int)r : 0;
+            p.hs_len = (int)seglen;
             if ((e = launch_bwd_bf16(p, s)) != hipSuccess)
                 return hip_status(e, "dilated bwd branch launch");
         }

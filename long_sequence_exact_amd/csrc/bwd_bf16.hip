@@ -174,9 +174,23 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const int k0 = kt * kBKV;
     const int kw0 = k0 + (wave & 3) * 32;
     const int key = kw0 + l32;  // this lane's key (accumulator column)
+    // rows of this head (fewer, and shifted, under head-dependent offsets,
+    // where the KV head has exactly one query head)
+    const HeadRows hr = head_rows(p.hs_r, p.hs_len, p.Nk, g);
+    const int Nk = hr.n, Nq = p.hs_r > 0 ? hr.n : p.Nq;
+    if (k0 >= Nk)
+        return;  // past this head's rows
 
-    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh;
-    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh;
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh +
+                    head_shift_elems(p.k, p.hs_r, hr.off);
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh +
+                    head_shift_elems(p.v, p.hs_r, hr.off);
+    // the same shift of the query-side views (all query heads of this
+    // workgroup share it)
+    const int64_t sq = head_shift_elems(p.q, p.hs_r, hr.off);
+    const int64_t so = head_shift_elems(p.dout, p.hs_r, hr.off);
+    const int64_t sl = head_shift_elems(p.lse, p.hs_r, hr.off);
+    const int64_t sd = head_shift_elems(p.dvec, p.hs_r, hr.off);
 
     // the wave's K rows (and, for dK, V rows) as B operands (k = d): lane
     // holds key `key`, d = 16kk + 8hl .. +8
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-        if (key < p.Nk) {
+        if (key < Nk) {
             xk = *(const u32x4 *)(K + (int64_t)key * p.k.sn + kk * 16 + hl * 8);
             if (is_dk)
                 xv = *(const u32x4 *)(V + (int64_t)key * p.v.sn + kk * 16 + hl * 8);
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 
     const float c = p.scale * kLog2e;
     const int group = p.Hq / p.Hkv;
-    const int nqt = (p.Nq + kBQ - 1) / kBQ;
+    const int nqt = (Nq + kBQ - 1) / kBQ;
     int qt_begin = 0;
     if (!p.noncausal) {
         const int first_q = max(0, k0 - p.delta);  // smallest query seeing key k0
@@ -224,10 +238,11 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     auto prefetch = [&](int it) {
         const int h = g * group + it / per_head;
         const int q0 = (qt_begin + it % per_head) * kBQ;
-        const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh;
-        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss + h * p.dout.sh;
-        const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2);
-        const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(p.Nq - 1) * p.dout.sn + D) * 2);
+        const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh + sq;
+        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss +
+                         h * p.dout.sh + so;
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(Nq - 1) * p.q.sn + D) * 2);
+        const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(Nq - 1) * p.dout.sn + D) * 2);
 #pragma unroll
         for (int u = 0; u < C::CPT; ++u) {
             qreg[u] = load16(qr, ((q0 + srow[u]) * (int)p.q.sn + scol[u]) * 2);
@@ -237,13 +252,13 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             const int i = q0 + tid;
             lreg = INFINITY;  // +inf: the row contributes P = 0
             dreg = 0.f;
-            if (i < p.Nq) {
+            if (i < Nq) {
                 const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
-                                   h * p.lse.sh + (int64_t)i * p.lse.sn);
+                                   h * p.lse.sh + sl + (int64_t)i * p.lse.sn);
                 if (lv != -INFINITY)
                     lreg = lv * kLog2e;
                 dreg = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss +
-                         h * p.dvec.sh + (int64_t)i * p.dvec.sn);
+                         h * p.dvec.sh + sd + (int64_t)i * p.dvec.sn);
             }
         }
     };
@@ -274,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             prefetch(it + 1);
 
         // ---- S = Q K^T (and dP = dO V^T for dK) for 2 blocks of 32 queries ----
-        const bool need_mask = (k0 + kBKV > p.Nk) || (q0 + kBQ > p.Nq) ||
+        const bool need_mask = (k0 + kBKV > Nk) || (q0 + kBQ > Nq) ||
                                (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
         unsigned pB[2][8];  // P (dV waves) or dS (dK waves), bf16 pairs
 #pragma unroll
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                     float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
                     if (need_mask) {
                         const int qi = q0 + r0 + u;
-                        const bool vis = key < p.Nk && qi < p.Nq &&
+                        const bool vis = key < Nk && qi < Nq &&
                                          (p.noncausal || key - qi <= p.delta);
                         pe = vis ? pe : 0.f;
                     }
@@ -343,12 +358,13 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     }
 
     // ---- write dK = sigma (dK^T)^T or dV (key rows, 4 consecutive d per store) ----
-    if (key >= p.Nk)
+    if (key >= Nk)
         return;
     const View &out = is_dk ? p.dk : p.dv;
     const int out_f32 = is_dk ? p.dk_f32 : p.dv_f32;
     const float f = is_dk ? p.scale : 1.f;
-    const int64_t krow = b * out.sb + s * out.ss + g * out.sh + (int64_t)key * out.sn;
+    const int64_t krow = b * out.sb + s * out.ss + g * out.sh +
+                         head_shift_elems(out, p.hs_r, hr.off) + (int64_t)key * out.sn;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -412,21 +428,30 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
     const int h = bsh % p.Hq, bs = bsh / p.Hq;
     const int s = bs % p.S, b = bs / p.S;
     const int g = (int)(((int64_t)h * p.Hkv) / p.Hq);
-
-    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh;
-    const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss + h * p.dout.sh;
-    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh;
-    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2);
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(p.Nq - 1) * p.dout.sn + D) * 2);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, ((int64_t)(p.Nk - 1) * p.k.sn + D) * 2);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, ((int64_t)(p.Nk - 1) * p.v.sn + D) * 2);
-
+    // rows of this head (fewer, and shifted, under head-dependent offsets)
+    const HeadRows hr = head_rows(p.hs_r, p.hs_len, p.Nq, h);
+    const int Nq = hr.n, Nk = p.hs_r > 0 ? hr.n : p.Nk;
     const int q0 = qt * kQBQ;
+    if (q0 >= Nq)
+        return;  // past this head's rows
+
+    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh +
+                    head_shift_elems(p.q, p.hs_r, hr.off);
+    const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss + h * p.dout.sh +
+                     head_shift_elems(p.dout, p.hs_r, hr.off);
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh +
+                    head_shift_elems(p.k, p.hs_r, hr.off);
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh +
+                    head_shift_elems(p.v, p.hs_r, hr.off);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(Nq - 1) * p.q.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(Nq - 1) * p.dout.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, ((int64_t)(Nk - 1) * p.k.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, ((int64_t)(Nk - 1) * p.v.sn + D) * 2);
+
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + l32;
 
-    int kv_end = p.Nk;
+    int kv_end = Nk;
     if (!p.noncausal)
         kv_end = min(kv_end, max(q0 + kQBQ + p.delta, 0));
     const int ntiles = (kv_end + BK - 1) / BK;
@@ -440,13 +465,14 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
         of[kk] = __builtin_bit_cast(bf16x8, load16(orr, (qrow * (int)p.dout.sn + kk * 16 + hl * 8) * 2));
     }
     float lse2 = INFINITY, dq_d = 0.f;  // +inf: the row contributes P = 0
-    if (qrow < p.Nq) {
+    if (qrow < Nq) {
         const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
-                           h * p.lse.sh + (int64_t)qrow * p.lse.sn);
+                           h * p.lse.sh + head_shift_elems(p.lse, p.hs_r, hr.off) +
+                           (int64_t)qrow * p.lse.sn);
         if (lv != -INFINITY)
             lse2 = lv * kLog2e;
         dq_d = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss + h * p.dvec.sh +
-                 (int64_t)qrow * p.dvec.sn);
+                 head_shift_elems(p.dvec, p.hs_r, hr.off) + (int64_t)qrow * p.dvec.sn);
     }
 
     f32x16 acc[D / 32];
@@ -508,7 +534,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
                 dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
             }
         }
-        const bool need_mask = (j0 + BK > p.Nk) ||
+        const bool need_mask = (j0 + BK > Nk) ||
                                (!p.noncausal && j0 + BK - 1 > q0w + p.delta);
         unsigned pS[BK / 32][8];
 #pragma unroll
@@ -521,7 +547,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
                     float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + u], c, -lse2));
                     if (need_mask) {
                         const int key = j0 + kb * 32 + ((e + u) >> 2) * 8 + hl * 4 + ((e + u) & 3);
-                        const bool vis = key < p.Nk && (p.noncausal || key - qrow <= p.delta);
+                        const bool vis = key < Nk && (p.noncausal || key - qrow <= p.delta);
                         pe = vis ? pe : 0.f;
                     }
                     ds[u] = pe * (dp[kb][e + u] - dq_d);
@@ -543,10 +569,10 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
         }
     }
 
-    if (qrow >= p.Nq)
+    if (qrow >= Nq)
         return;
     float *dQ = (float *)p.dq.ptr + b * p.dq.sb + s * p.dq.ss + h * p.dq.sh +
-                (int64_t)qrow * p.dq.sn;
+                head_shift_elems(p.dq, p.hs_r, hr.off) + (int64_t)qrow * p.dq.sn;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll

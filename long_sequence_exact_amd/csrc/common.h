@@ -25,6 +25,12 @@ struct FwdParams {
     float scale;         // softmax scale (natural units)
     int accumulate;      // fused LSE-merge epilogue into fp32 (o, lse)
     int o_f32;           // output element type: 1 fp32, 0 bf16
+    // Head-dependent dilation offsets (0: none).  With hs_r = r > 0 the views
+    // select every r-th row of a segment of hs_len rows (row stride r times
+    // the tensor's), and query head h starts at row h mod r of the segment:
+    // its views move by that many tensor rows and hold
+    // ceil((hs_len - h mod r) / r) rows; Nq = Nk is the count at offset 0.
+    int hs_r = 0, hs_len = 0;
 };
 
 struct MergeParams {
@@ -43,7 +49,31 @@ struct BwdParams {
     float scale;
     int o_f32, dk_f32, dv_f32;
     int acc_kv;            // 1: dk, dv (fp32) are accumulated instead of written
+    int hs_r = 0, hs_len = 0;  // head-dependent offsets as in FwdParams; query
+                           // head h = KV head (one query head per KV head)
 };
+
+// Rows and row shift of head h under head-dependent dilation offsets
+// (hs_r > 0); n0 rows and no shift otherwise.
+struct HeadRows {
+    int n;    // selected rows of this head
+    int off;  // offset inside the segment, in tensor rows
+};
+__host__ __device__ inline HeadRows head_rows(int hs_r, int hs_len, int n0, int h)
+{
+    if (hs_r <= 0)
+        return {n0, 0};
+    const int off = h % hs_r;
+    const int n = hs_len > off ? (hs_len - off + hs_r - 1) / hs_r : 0;
+    return {n, off};
+}
+
+// Element shift of a view's first row for offset `off` (its row stride is
+// hs_r tensor rows; the kernels address rows with 32-bit strides).
+__host__ __device__ inline int64_t head_shift_elems(const View &v, int hs_r, int off)
+{
+    return hs_r > 0 ? (int64_t)off * ((int)v.sn / hs_r) : 0;
+}
 
 // Copy of (flat head f, row n) vectors between two strided layouts; strides
 // in bytes, a vector is `units` 16-byte units.  f = b * src_h + h on the

@@ -134,20 +134,28 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     const int bs = bh / p.Hq;
     const int s = bs % p.S, b = bs / p.S;
     const int g = (int)(((int64_t)h * p.Hkv) / p.Hq);
-
-    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh;
-    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh;
-    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh;
-    // valid bytes of each view: rows past Nq / Nk read as zeros
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, p.Nq > 0 ? ((int64_t)(p.Nq - 1) * p.q.sn + D) * 2 : 0);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, p.Nk > 0 ? ((int64_t)(p.Nk - 1) * p.k.sn + D) * 2 : 0);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, p.Nk > 0 ? ((int64_t)(p.Nk - 1) * p.v.sn + D) * 2 : 0);
-
+    // rows of this head (fewer, and shifted, under head-dependent offsets)
+    const HeadRows hr = head_rows(p.hs_r, p.hs_len, p.Nq, h);
+    const int Nq = hr.n, Nk = p.hs_r > 0 ? hr.n : p.Nk;
     const int q0 = qt * kBQ;
+    if (q0 >= Nq)
+        return;  // past this head's rows
+    const int64_t rq = head_shift_elems(p.q, p.hs_r, hr.off);
+    const int64_t rk = head_shift_elems(p.k, p.hs_r, hr.off);
+    const int64_t rv = head_shift_elems(p.v, p.hs_r, hr.off);
+
+    const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh + rq;
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh + rk;
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh + rv;
+    // valid bytes of each view: rows past Nq / Nk read as zeros
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(Nq - 1) * p.q.sn + D) * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, Nk > 0 ? ((int64_t)(Nk - 1) * p.k.sn + D) * 2 : 0);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, Nk > 0 ? ((int64_t)(Nk - 1) * p.v.sn + D) * 2 : 0);
+
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + l32;
 
-    int kv_end = p.Nk;
+    int kv_end = Nk;
     if (!p.noncausal) {
         const int lim = q0 + kBQ + p.delta;  // keys < lim can be visible
         kv_end = min(kv_end, max(lim, 0));
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 
         // accumulator element e of block kb: key j0 + 32kb + 8(e/4) + 4hl + e%4,
         // query qrow
-        const bool need_mask = (j0 + BK > p.Nk) ||
+        const bool need_mask = (j0 + BK > Nk) ||
                                (!p.noncausal && j0 + BK - 1 > q0w + p.delta);
         if (need_mask) {
 #pragma unroll
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = j0 + kb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-                    const bool vis = key < p.Nk && (p.noncausal || key - qrow <= p.delta);
+                    const bool vis = key < Nk && (p.noncausal || key - qrow <= p.delta);
                     if (!vis)
                         sacc[kb][e] = -INFINITY;
                 }
@@ -324,12 +332,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     const bool has = l_tot > 0.f;
     const float inv = has ? 1.f / l_tot : 0.f;
     const float lse_new = has ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if (qrow >= p.Nq)
+    if (qrow >= Nq)
         return;
 
-    float *Lp = (float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss + h * p.lse.sh +
+    const int64_t ro = head_shift_elems(p.o, p.hs_r, hr.off);
+    const int64_t rl = head_shift_elems(p.lse, p.hs_r, hr.off);
+    float *Lp = (float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss + h * p.lse.sh + rl +
                 (int64_t)qrow * p.lse.sn;
-    const int64_t orow = b * p.o.sb + s * p.o.ss + h * p.o.sh + (int64_t)qrow * p.o.sn;
+    const int64_t orow = b * p.o.sb + s * p.o.ss + h * p.o.sh + ro + (int64_t)qrow * p.o.sn;
 
     if (!p.accumulate) {
         if (hl == 0)
