@@ -110,6 +110,21 @@ __device__ inline int vswz(int row)
     return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+// Max and sum of x over lanes l and l ^ 32 (the two halves of a query's
+// column in the 32x32 accumulator) without the LDS crossbar: permlane32_swap
+// with x in both operands returns, in every lane, x of lane l & 31 and x of
+// lane (l & 31) + 32, so both halves form the same value.
+__device__ inline float lane_pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float lane_pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 {
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 mx = fmaxf(mx, sacc[kb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = lane_pair_max(mx);
 
         // conditional rescale: raise the reference max only when some score
         // exceeds it by more than the slack (always on a row's first keys)
@@ -328,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l), optional merge ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = lane_pair_sum(l_run);
     const bool has = l_tot > 0.f;
     const float inv = has ? 1.f / l_tot : 0.f;
     const float lse_new = has ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
