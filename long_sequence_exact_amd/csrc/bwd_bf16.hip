@@ -114,7 +114,6 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(View x, int B, int H, int
 
 template <int D>
 struct BCfg {
-    static constexpr int QSTR = D + 8;         // Q / dO row pitch (bf16)
     static constexpr int CPT = kBQ * D / 8 / kThreads;  // 16-byte chunks per thread per tile
     static_assert(CPT * kThreads * 8 == kBQ * D, "tile split");
 };
@@ -148,12 +147,34 @@ __device__ inline bf16x8 cat_tr(v4i16 lo, v4i16 hi)
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The Q / dO tiles (dK/dV kernel) and the K tile (dQ kernel) are read two
+// ways: as MFMA row operands (a read phase = 16 consecutive rows x one
+// 16-byte chunk) and by transposing reads (a phase = 4 consecutive rows x 4
+// chunks).  Rows are unpadded (D/8 chunks of 16 bytes); logical chunk c of
+// row r sits at c ^ tswz(r).  The swizzle is a bijection on the 16 (d = 128)
+// or, per row parity, 8 (d = 64) rows of a phase of the first kind and puts
+// each of 4 consecutive rows in a different 64-byte bank group, so neither
+// kind of read conflicts.
+template <int D>
+__device__ inline int tswz(int row)
+{
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                    : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// byte offset of logical chunk c of row r in a swizzled tile
+template <int D>
+__device__ inline int swz_off(int r, int c)
+{
+    return r * (2 * D) + ((c ^ tswz<D>(r)) << 4);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 {
     using C = BCfg<D>;
-    __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * C::QSTR];
-    __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * C::QSTR];
+    __shared__ __attribute__((aligned(16))) char Qs[kBQ * 2 * D];
+    __shared__ __attribute__((aligned(16))) char dOs[kBQ * 2 * D];
     __shared__ float lse2s[kBQ];
     __shared__ float Dsh[kBQ];
 
@@ -265,8 +286,10 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 
     // transposing-read offset (see read_tr) of the Q^T / dO^T operands, in the
     // query order of the P / dS accumulator rows
-    const int tq_off = (4 * (gg >> 1) + (ip >> 2)) * C::QSTR + 16 * (gg & 1) + 4 * (ip & 3);
-    const bf16 *At = is_dk ? Qs : dOs;  // A operand of dK^T += Q^T dS / dV^T += dO^T P
+    // (row 4 (gg/2) + ip/4 + 8 rr + 16 ks, chunk 4 i + 2 (gg%2) + (ip%4)/2,
+    // 8-byte half ip%2)
+    const int trow = 4 * (gg >> 1) + (ip >> 2);
+    const char *At = is_dk ? Qs : dOs;  // A operand of dK^T += Q^T dS / dV^T += dO^T P
 
     if (niters > 0)
         prefetch(0);
@@ -277,8 +300,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         __syncthreads();  // previous iteration done with Qs, dOs
 #pragma unroll
         for (int u = 0; u < C::CPT; ++u) {
-            *(u32x4 *)(&Qs[srow[u] * C::QSTR + scol[u]]) = qreg[u];
-            *(u32x4 *)(&dOs[srow[u] * C::QSTR + scol[u]]) = oreg[u];
+            *(u32x4 *)(Qs + swz_off<D>(srow[u], scol[u] >> 3)) = qreg[u];
+            *(u32x4 *)(dOs + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
         }
         if (tid < kBQ) {
             lse2s[tid] = lreg;
@@ -300,13 +323,13 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                 s[e] = dp[e] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 aq = *(const bf16x8 *)(&Qs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                const bf16x8 aq = *(const bf16x8 *)(Qs + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
             }
             if (is_dk) {
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
-                    const bf16x8 ad = *(const bf16x8 *)(&dOs[(qb * 32 + l32) * C::QSTR + kk * 16 + hl * 8]);
+                    const bf16x8 ad = *(const bf16x8 *)(dOs + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
                 }
             }
@@ -350,8 +373,10 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             const bf16x8 bb = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const int off = (16 * ks) * C::QSTR + 32 * i + tq_off;
-                const bf16x8 a = cat_tr(read_tr(&At[off]), read_tr(&At[off + 8 * C::QSTR]));
+                const int c = 4 * i + 2 * (gg & 1) + ((ip & 3) >> 1);
+                const int o0 = swz_off<D>(16 * ks + trow, c) + (ip & 1) * 8;
+                const int o1 = swz_off<D>(16 * ks + 8 + trow, c) + (ip & 1) * 8;
+                const bf16x8 a = cat_tr(read_tr((const bf16 *)(At + o0)), read_tr((const bf16 *)(At + o1)));
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[i], 0, 0, 0);
             }
         }
@@ -403,7 +428,6 @@ constexpr int kQBQ = 32 * kQWaves;
 template <int D>
 struct QCfg {
     static constexpr int BK = 64;               // keys per tile
-    static constexpr int STR = D + 8;           // K / V row pitch (bf16)
     static constexpr int CPT = BK * D / 8 / kQThreads;  // 16-byte chunks per thread per tile
     static_assert(CPT * kQThreads * 8 == BK * D, "tile split");
 };
@@ -413,8 +437,8 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
 {
     using C = QCfg<D>;
     constexpr int BK = C::BK;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[BK * C::STR];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[BK * C::STR];
+    __shared__ __attribute__((aligned(16))) char Ks[BK * 2 * D];
+    __shared__ __attribute__((aligned(16))) char Vs[BK * 2 * D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -501,15 +525,15 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
     };
     // transposing-read offset of the K^T operand, in the key order of the
     // dS^T accumulator rows
-    const int tk_off = (4 * (gg >> 1) + (ip >> 2)) * C::STR + 16 * (gg & 1) + 4 * (ip & 3);
+    const int trow = 4 * (gg >> 1) + (ip >> 2);
 
     load_tile(0);
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < C::CPT; ++u) {
-            *(u32x4 *)(&Ks[srow[u] * C::STR + scol[u]]) = kreg[u];
-            *(u32x4 *)(&Vs[srow[u] * C::STR + scol[u]]) = vreg[u];
+            *(u32x4 *)(Ks + swz_off<D>(srow[u], scol[u] >> 3)) = kreg[u];
+            *(u32x4 *)(Vs + swz_off<D>(srow[u], scol[u] >> 3)) = vreg[u];
         }
         __syncthreads();
         if (t + 1 < ntiles)
@@ -527,9 +551,9 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
                 s[kb][e] = dp[kb][e] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                const int off = (kb * 32 + l32) * C::STR + kk * 16 + hl * 8;
-                const bf16x8 ak = *(const bf16x8 *)(&Ks[off]);
-                const bf16x8 av = *(const bf16x8 *)(&Vs[off]);
+                const int off = swz_off<D>(kb * 32 + l32, 2 * kk + hl);
+                const bf16x8 ak = *(const bf16x8 *)(Ks + off);
+                const bf16x8 av = *(const bf16x8 *)(Vs + off);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], s[kb], 0, 0, 0);
                 dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
             }
@@ -562,8 +586,10 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
             const bf16x8 bs = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const int off = (16 * ks) * C::STR + 32 * i + tk_off;
-                const bf16x8 a = cat_tr(read_tr(&Ks[off]), read_tr(&Ks[off + 8 * C::STR]));
+                const int c = 4 * i + 2 * (gg & 1) + ((ip & 3) >> 1);
+                const int o0 = swz_off<D>(16 * ks + trow, c) + (ip & 1) * 8;
+                const int o1 = swz_off<D>(16 * ks + 8 + trow, c) + (ip & 1) * 8;
+                const bf16x8 a = cat_tr(read_tr((const bf16 *)(Ks + o0)), read_tr((const bf16 *)(Ks + o1)));
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[i], 0, 0, 0);
             }
         }
