@@ -114,8 +114,11 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(View x, int B, int H, int
 
 template <int D>
 struct BCfg {
-    static constexpr int CPT = kBQ * D / 8 / kThreads;  // 16-byte chunks per thread per tile
-    static_assert(CPT * kThreads * 8 == kBQ * D, "tile split");
+    // query rows per iteration: 128 at d = 64, where one step's contractions
+    // are half as long, so barriers and staging weigh as much as at d = 128
+    static constexpr int BQ = D == 64 ? 2 * kBQ : kBQ;
+    static constexpr int CPT = BQ * D / 8 / kThreads;  // 16-byte chunks per thread per tile
+    static_assert(CPT * kThreads * 8 == BQ * D, "tile split");
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -173,10 +176,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 {
     using C = BCfg<D>;
-    __shared__ __attribute__((aligned(16))) char Qs[kBQ * 2 * D];
-    __shared__ __attribute__((aligned(16))) char dOs[kBQ * 2 * D];
-    __shared__ float lse2s[kBQ];
-    __shared__ float Dsh[kBQ];
+    constexpr int BQ = C::BQ;
+    __shared__ __attribute__((aligned(16))) char Qs[BQ * 2 * D];
+    __shared__ __attribute__((aligned(16))) char dOs[BQ * 2 * D];
+    __shared__ float lse2s[BQ];
+    __shared__ float Dsh[BQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -237,11 +241,11 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 
     const float c = p.scale * kLog2e;
     const int group = p.Hq / p.Hkv;
-    const int nqt = (Nq + kBQ - 1) / kBQ;
+    const int nqt = (Nq + BQ - 1) / BQ;
     int qt_begin = 0;
     if (!p.noncausal) {
         const int first_q = max(0, k0 - p.delta);  // smallest query seeing key k0
-        qt_begin = min(nqt, first_q / kBQ);
+        qt_begin = min(nqt, first_q / BQ);
     }
     const int per_head = nqt - qt_begin;
     const int niters = group * per_head;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     }
     auto prefetch = [&](int it) {
         const int h = g * group + it / per_head;
-        const int q0 = (qt_begin + it % per_head) * kBQ;
+        const int q0 = (qt_begin + it % per_head) * BQ;
         const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh + sq;
         const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss +
                          h * p.dout.sh + so;
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             qreg[u] = load16(qr, ((q0 + srow[u]) * (int)p.q.sn + scol[u]) * 2);
             oreg[u] = load16(orr, ((q0 + srow[u]) * (int)p.dout.sn + scol[u]) * 2);
         }
-        if (tid < kBQ) {
+        if (tid < BQ) {
             const int i = q0 + tid;
             lreg = INFINITY;  // +inf: the row contributes P = 0
             dreg = 0.f;
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         prefetch(0);
 
     for (int it = 0; it < niters; ++it) {
-        const int q0 = (qt_begin + it % per_head) * kBQ;
+        const int q0 = (qt_begin + it % per_head) * BQ;
 
         __syncthreads();  // previous iteration done with Qs, dOs
 #pragma unroll
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             *(u32x4 *)(Qs + swz_off<D>(srow[u], scol[u] >> 3)) = qreg[u];
             *(u32x4 *)(dOs + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
         }
-        if (tid < kBQ) {
+        if (tid < BQ) {
             lse2s[tid] = lreg;
             Dsh[tid] = dreg;
         }
@@ -311,12 +315,12 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         if (it + 1 < niters)
             prefetch(it + 1);
 
-        // ---- S = Q K^T (and dP = dO V^T for dK) for 2 blocks of 32 queries ----
-        const bool need_mask = (k0 + kBKV > Nk) || (q0 + kBQ > Nq) ||
+        // ---- S = Q K^T (and dP = dO V^T for dK) for BQ / 32 blocks of 32 queries ----
+        const bool need_mask = (k0 + kBKV > Nk) || (q0 + BQ > Nq) ||
                                (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
-        unsigned pB[2][8];  // P (dV waves) or dS (dK waves), bf16 pairs
+        unsigned pB[BQ / 32][8];  // P (dV waves) or dS (dK waves), bf16 pairs
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < BQ / 32; ++qb) {
             f32x16 s, dp;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -364,9 +368,9 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             }
         }
 
-        // ---- dV^T += dO^T P or dK^T += Q^T dS (k = the tile's 64 query rows) ----
+        // ---- dV^T += dO^T P or dK^T += Q^T dS (k = the tile's BQ query rows) ----
 #pragma unroll
-        for (int ks = 0; ks < kBQ / 16; ++ks) {
+        for (int ks = 0; ks < BQ / 16; ++ks) {
             const int qb = ks >> 1, half = ks & 1;
             u32x4 w = {pB[qb][half * 4 + 0], pB[qb][half * 4 + 1], pB[qb][half * 4 + 2],
                        pB[qb][half * 4 + 3]};
@@ -427,7 +431,7 @@ constexpr int kQBQ = 32 * kQWaves;
 
 template <int D>
 struct QCfg {
-    static constexpr int BK = 64;               // keys per tile
+    static constexpr int BK = D == 64 ? 128 : 64;  // keys per tile (same bytes for both d)
     static constexpr int CPT = BK * D / 8 / kQThreads;  // 16-byte chunks per thread per tile
     static_assert(CPT * kQThreads * 8 == BK * D, "tile split");
 };
