@@ -191,3 +191,28 @@ def test_bwd_empty_and_fully_masked_segments():
     _, dk2, dv2 = sa.attn_segment_bwd(qz, k, v, o[..., :0, :], lse[..., :0], do[..., :0, :])
     torch.cuda.synchronize()
     assert torch.all(dk2 == 0) and torch.all(dv2 == 0)
+
+
+def test_largest_query_extent():
+    """One query head whose Q, dO (and fp32 O, dQ rows) span the largest extent
+    the library accepts (8,388,088 rows of d = 128, just under 2 GiB of bf16
+    per head, addressed with 32-bit byte offsets) against 200 keys,
+    non-causal: dQ on sampled rows, including the last, against the oracle;
+    dK and dV through sum_j dV_j = sum_i dO_i and sum_j dK_j = 0."""
+    d = 128
+    nq = (1 << 31) // (2 * d) - 512 - 8
+    nk = 200
+    q, k, v, do = draw([(1, 1, nq, d), (1, 1, nk, d), (1, 1, nk, d), (1, 1, nq, d)], 2600)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = sa.attn_segment_fwd(qd, kd, vd, out_dtype=torch.float32)
+    dq, dk, dv = sa.attn_segment_bwd(qd, kd, vd, o, lse, dod)
+    torch.cuda.synchronize()
+    rows = np.array(sample_rows(nq, 4, 2601, must=(0, nq - 1)), np.int64)
+    ref, _, _ = oracle.attn_bwd_dq_rows(_np32(q), _np32(k), _np32(v), _np32(do), rows=rows)
+    e = normwise_per_head(to_np(dq[0, 0, torch.from_numpy(rows).to(DEV)]), ref,
+                          np.zeros(len(rows), np.int64))
+    assert e <= BTOL, f"largest query extent: sampled dq error {e:.3e}"
+    sdo = do[0, 0].double().sum(0)
+    assert (dv[0, 0].double().sum(0).cpu() - sdo).abs().max() <= BTOL * sdo.abs().max()
+    mag = dk[0, 0].double().abs().sum(0).cpu().max()
+    assert dk[0, 0].double().sum(0).abs().max().cpu() <= 1e-3 * mag

@@ -251,6 +251,25 @@ def _sampled_check(q, k, v, o, lse, delta, rows_per_head, seed, must_rows=(0, -1
     return o_g, l_g, o_ref, l_ref, rows // N
 
 
+def test_largest_key_extent_sampled():
+    """One head whose K and V each span just under 2 GiB (8,388,088 rows of
+    d = 128, the largest extent the library accepts, since it addresses a
+    head's rows with 32-bit byte offsets), 260 query rows seeing all keys but
+    the last few: sampled rows against the oracle, so the offsets near 2^31
+    are read correctly."""
+    d = 128
+    nk = (1 << 31) // (2 * d) - 512 - 8
+    nq = 260
+    delta = nk - 300
+    q, k, v = draw([(1, 1, nq, d), (1, 1, nk, d), (1, 1, nk, d)], 1300)
+    o, lse = sa.attn_segment_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal_offset=delta,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    og, lg, orf, lrf, heads = _sampled_check(q, k, v, o, lse, delta, 3, 1301,
+                                             must_rows=(0, 259))
+    assert_parity(og, lg, orf, lrf, torch.bfloat16, rows_heads=heads, what="2 GiB keys")
+
+
 def test_ring_16k_full_size_sampled():
     """32 heads, d=128, 16384 tokens, causal, 8 ranks x 2048 rows swept over 8
     KV segments with fused merges; sampled rows against the oracle."""
