@@ -43,6 +43,7 @@ int64_t numel(const seqattn_tensor *t) { return t->b * t->h * t->n * t->d; }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 constexpr int64_t kMaxBH = (int64_t)1 << 20;
+constexpr int64_t kMaxStride = (int64_t)1 << 40;  // elements; keeps every extent in int64
 
 // Structural checks of one descriptor: non-null, known dtype, non-negative
 // dims within range, non-negative strides, 16-byte row alignment (rows, d>1).
@@ -54,10 +55,21 @@ int check_tensor(const seqattn_tensor *t, const char *name, bool is_lse)
         return fail(SEQATTN_ERR_DTYPE, "%s: unknown dtype %d", name, (int)t->dtype);
     if (t->b < 0 || t->h < 0 || t->n < 0 || t->d < 0)
         return fail(SEQATTN_ERR_SHAPE, "%s: negative dimension", name);
-    if (t->n >= kMaxRows || t->b * t->h >= kMaxBH || t->b >= kMaxBH || t->h >= kMaxBH)
+    if (t->n >= kMaxRows || t->d >= kMaxRows || t->b >= kMaxBH || t->h >= kMaxBH ||
+        t->b * t->h >= kMaxBH)
         return fail(SEQATTN_ERR_SHAPE, "%s: dimension too large", name);
     if (t->stride_b < 0 || t->stride_h < 0 || t->stride_n < 0)
         return fail(SEQATTN_ERR_STRIDE, "%s: negative stride", name);
+    if (t->stride_b >= kMaxStride || t->stride_h >= kMaxStride || t->stride_n >= kMaxStride)
+        return fail(SEQATTN_ERR_STRIDE, "%s: stride too large", name);
+    if (numel(t) > 0) {
+        // the byte span, which overlap tests and offsets below take in 64 bits
+        const __int128 span = ((__int128)(t->b - 1) * t->stride_b +
+                               (__int128)(t->h - 1) * t->stride_h +
+                               (__int128)(t->n - 1) * t->stride_n + t->d) * esize(t->dtype);
+        if (span >= ((__int128)1 << 56))
+            return fail(SEQATTN_ERR_STRIDE, "%s: spans 2^56 bytes or more", name);
+    }
     if (numel(t) > 0 && t->data == nullptr)
         return fail(SEQATTN_ERR_NULL, "%s: data pointer is NULL", name);
     if (is_lse) {
@@ -216,8 +228,9 @@ hipStream_t stream_of(void *s) { return (hipStream_t)s; }
 // plus the tile overrun of the last tile, must span less than 2 GiB.
 int check_head_extent(const seqattn_tensor *t, const char *name, int64_t row_step)
 {
-    const int64_t rows = t->n + 512 * row_step;
-    if (rows * t->stride_n * esize(t->dtype) >= ((int64_t)1 << 31))
+    // rows < 2^31 + 2^29 and stride_n * esize < 2^42: the product fits in 128 bits
+    const __int128 rows = (__int128)t->n + 512 * (__int128)row_step;
+    if (rows * t->stride_n * esize(t->dtype) >= ((__int128)1 << 31))
         return fail(SEQATTN_ERR_UNSUPPORTED, "%s: one head spans >= 2 GiB", name);
     return SEQATTN_OK;
 }
@@ -510,7 +523,9 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
         return fail(SEQATTN_ERR_UNSUPPORTED, "backward takes bf16 q/k/v");
     if (d_o->dtype != SEQATTN_BF16)
         return fail(SEQATTN_ERR_DTYPE, "d_o must be bf16");
-    if ((st = check_head_extent(q, "q", 1)) || (st = check_head_extent(d_o, "d_o", 1)))
+    // the dQ kernel also reads K and V tiles with 32-bit offsets
+    if ((st = check_head_extent(q, "q", 1)) || (st = check_head_extent(d_o, "d_o", 1)) ||
+        (st = check_head_extent(k, "k", 1)) || (st = check_head_extent(v, "v", 1)))
         return st;
     if (dq->dtype != SEQATTN_F32)
         return fail(SEQATTN_ERR_DTYPE, "dq must be fp32 (accumulated)");

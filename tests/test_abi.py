@@ -111,6 +111,27 @@ def test_fwd_validation_errors(L):
     assert L.seqattn_status_string(EALIAS).decode() == "output aliases an input"
 
 
+def test_oversized_dimensions_and_strides_are_rejected(L):
+    q, k, v, o, lse = qkvo()
+    # b * h would overflow int64 if multiplied first
+    huge = T(BASE, _lib.BF16, 1 << 40, 1 << 40, 256, 128)
+    assert fwd(L, huge, k, v, o, lse) == ESHAPE
+    # a stride beyond 2^40 elements
+    far = T(BASE, _lib.BF16, 2, 4, 256, 128, stride_b=1 << 50)
+    assert fwd(L, far, k, v, o, lse) == ESTRIDE
+    # rows x row stride beyond 2^64 bytes: rejected, not wrapped around
+    wide = T(BASE, _lib.BF16, 1, 4, (1 << 30) - 1, 128, stride_n=(1 << 39))
+    assert fwd(L, wide, k, v, o, lse) == ESTRIDE
+    assert "2^56" in L.seqattn_last_error().decode()
+    # a head spanning 16 GiB through its row stride: the 2 GiB per-head limit
+    q1, k1, v1, o1, l1 = qkvo(hq=1, hkv=1, nq=1 << 20)
+    tall = T(BASE, _lib.BF16, 1, 1, 1 << 20, 128, stride_n=8192, stride_h=8192 << 20)
+    o1 = T(BASE + (1 << 40), _lib.BF16, 1, 1, 1 << 20, 128)
+    l1 = LSE(BASE + (2 << 40), 1, 1, 1 << 20)
+    assert fwd(L, tall, k1, v1, o1, l1) == EUNSUP
+    assert "2 GiB" in L.seqattn_last_error().decode()
+
+
 def test_fwd_empty_query_block_returns_ok_without_launch(L):
     q, k, v, o, lse = qkvo(nq=0)
     assert fwd(L, q, k, v, o, lse) == OK
@@ -182,6 +203,15 @@ def test_bwd_validation_errors(L):
     qf, kf, vf, _, _ = qkvo(dtype=_lib.F32)
     assert L.seqattn_attn_segment_bwd(r(qf), r(kf), r(vf), r(o), r(lse), r(do), 0, 0.0, 0,
                                       r(dq), r(dk), r(dv), ws, need, None) == EUNSUP
+    # K / V heads spanning 2 GiB: the dQ kernel addresses them with 32-bit offsets
+    nbig = (1 << 31) // 256
+    kb = T(BASE + step, _lib.BF16, 1, 2, nbig, 128)
+    vb = T(BASE + 40 * step, _lib.BF16, 1, 2, nbig, 128)
+    dkb = T(BASE + 80 * step, _lib.F32, 1, 2, nbig, 128)
+    dvb = T(BASE + 120 * step, _lib.F32, 1, 2, nbig, 128)
+    assert L.seqattn_attn_segment_bwd(r(q), r(kb), r(vb), r(o), r(lse), r(do), 0, 0.0, 0,
+                                      r(dq), r(dkb), r(dvb), ws, need, None) == EUNSUP
+    assert "2 GiB" in L.seqattn_last_error().decode()
 
 
 def test_dilated_bwd_validation_errors(L):
