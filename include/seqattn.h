@@ -111,7 +111,10 @@ typedef struct {
  * Nq = 0 or Nk = 0 is allowed (an empty segment leaves an accumulator
  * unchanged and writes (0, -inf) otherwise).
  * Errors: NULL, DTYPE, SHAPE (d not 64/128, batch mismatch, Hq % Hkv != 0,
- * lse shape), STRIDE, ALIAS (o or lse overlapping q/k/v), HIP.
+ * lse shape), STRIDE (misalignment, overlapping rows, a tensor spanning 2^56
+ * bytes), ALIAS (o or lse overlapping q/k/v), UNSUPPORTED (bf16: one head of
+ * q, k or v spanning 2 GiB or more, since the kernels address a head's rows
+ * with 32-bit byte offsets; unknown flags), HIP.
  */
 int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              const seqattn_tensor *v, int64_t causal_offset,
@@ -163,7 +166,8 @@ int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
  * dilations[i] >= 1 (host arrays of n_branches >= 1 entries).
  * workspace: when o is bf16, seqattn_workspace_size(SEQATTN_OP_DILATED_FWD)
  * bytes of device memory (an fp32 accumulator); may be NULL when o is fp32.
- * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, WORKSPACE, HIP.
+ * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, WORKSPACE, UNSUPPORTED (a head
+ * of q, k or v spanning about 2 GiB, unknown flags), HIP.
  */
 int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              const seqattn_tensor *v,
@@ -196,7 +200,8 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
  * (flags 0) or, with SEQATTN_ACCUMULATE, fp32 and ACCUMULATED.
  * workspace: seqattn_workspace_size(SEQATTN_OP_SEGMENT_BWD) bytes.
  * Errors: NULL, DTYPE, SHAPE, STRIDE, ALIAS, WORKSPACE, UNSUPPORTED (fp32
- * inputs, unknown flags), HIP.
+ * inputs, unknown flags, one head of q, k, v or d_o spanning 2 GiB or more),
+ * HIP.
  */
 int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              const seqattn_tensor *v, const seqattn_tensor *o,
