@@ -70,8 +70,8 @@ def lse_merge(o_acc, lse_acc, o_b, lse_b):
 
 def workspace_size(op: int, q, other) -> int:
     L = _lib.lib()
-    a = _lib.desc(q)
-    b = _lib.desc(other)
+    a = _lib.desc(q, on_device=False)
+    b = _lib.desc(other, on_device=False)
     return int(L.seqattn_workspace_size(op, ctypes.byref(a), ctypes.byref(b), 0))
 
 
@@ -103,6 +103,8 @@ def dilated_attn_fwd(q, k, v, segment_lengths, dilations, causal=False, scale=No
                                         ctypes.byref(dod), n))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must be on the GPU")
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(L.seqattn_dilated_attn_fwd(
@@ -137,6 +139,8 @@ def attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, scale=None, dq=No
                                         ctypes.byref(ds[1]), 0))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must be on the GPU")
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(L.seqattn_attn_segment_bwd(
@@ -174,6 +178,8 @@ def dilated_attn_bwd(q, k, v, o, lse, d_o, segment_lengths, dilations, causal=Fa
                                         ctypes.byref(ds[1]), n))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must be on the GPU")
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(L.seqattn_dilated_attn_bwd(

@@ -86,8 +86,12 @@ def check(status: int):
                                    f"{L.seqattn_last_error().decode()}")
 
 
-def desc(t: torch.Tensor, lse: bool = False) -> Tensor:
-    """Descriptor of a [B,H,N,d] / [H,N,d] tensor, or of an LSE [B,H,N] / [H,N]."""
+def desc(t: torch.Tensor, lse: bool = False, on_device: bool = True) -> Tensor:
+    """Descriptor of a [B,H,N,d] / [H,N,d] tensor, or of an LSE [B,H,N] / [H,N].
+    The kernels read and write these addresses, so they must be GPU memory
+    (on_device=False only for size queries)."""
+    if on_device and not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
     if t.dtype == torch.bfloat16:
         dt = BF16
     elif t.dtype == torch.float32:

@@ -149,3 +149,17 @@ def test_stream_lanes_partition_every_rank_batch(lanes):
             assert all((first + b) % lanes == lane for b in entries)
             seen += entries
         assert sorted(seen) == list(range(count))
+
+
+def test_binding_rejects_host_tensors():
+    # the kernels dereference these addresses: a host tensor must be refused
+    # before anything reaches the library
+    import long_sequence_exact_amd as sa
+    x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sa.attn_segment_fwd(x, x, x, out=torch.empty(x.shape), lse=torch.empty(x.shape[:-1]))
+    with pytest.raises(ValueError, match="GPU"):
+        sa.lse_merge(torch.zeros((1, 1, 8, 64)), torch.zeros((1, 1, 8)),
+                     torch.zeros((1, 1, 8, 64)), torch.zeros((1, 1, 8)))
+    # size queries take host descriptors
+    assert sa.workspace_size(3, x, x) == 8 * 4
