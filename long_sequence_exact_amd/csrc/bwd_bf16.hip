@@ -330,12 +330,27 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                 const bf16x8 aq = *(const bf16x8 *)(Qs + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
             }
+            // keep four operand reads in flight ahead of the MFMA that uses them
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int u = 0; u < D / 16 - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             if (is_dk) {
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
                     const bf16x8 ad = *(const bf16x8 *)(dOs + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int u = 0; u < D / 16 - 4; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
             // element e: query row qb*32 + 8(e/4) + 4hl + e%4 of the tile
 #pragma unroll
@@ -384,6 +399,14 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[i], 0, 0, 0);
             }
         }
+        // two transposing reads per MFMA; keep four MFMAs' worth in flight
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < (BQ / 16) * (D / 32) - 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     // ---- write dK = sigma (dK^T)^T or dV (key rows, 4 consecutive d per store) ----
@@ -562,6 +585,14 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
                 dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
             }
         }
+        // keep four operand reads in flight ahead of the MFMA that uses them
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int u = 0; u < 2 * (BK / 32) * (D / 16) - 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         const bool need_mask = (j0 + BK > Nk) ||
                                (!p.noncausal && j0 + BK - 1 > q0w + p.delta);
         unsigned pS[BK / 32][8];
@@ -597,6 +628,14 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, acc[i], 0, 0, 0);
             }
         }
+        // two transposing reads per MFMA; keep four MFMAs' worth in flight
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < (BK / 16) * (D / 32) - 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     if (qrow >= Nq)
