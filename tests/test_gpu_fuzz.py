@@ -1,7 +1,8 @@
 """Seeded random sweep against the fp64 oracle: shapes, causal offsets, head
 groupings, layouts and flags drawn by one generator, for the segment forward
 (bf16 and fp32, with and without the fused merge), its backward and dilated
-attention (forward and backward, with and without head-dependent offsets).
+attention (forward and backward, with and without head-dependent offsets),
+batch 1 or 2.
 
 Each case prints its parameters in the assertion message, so a failure names
 the case; the draw is deterministic (numpy generator, fixed seed).
@@ -45,15 +46,16 @@ def _fwd_cases(count, seed):
         split = int(rng.integers(1, nk)) if (nk > 1 and rng.random() < 0.35) else 0
         out_bf16 = dtype == torch.bfloat16 and split == 0 and rng.random() < 0.5
         seq_major = bool(rng.random() < 0.3)
-        out.append((i, d, hkv, group, nq, nk, delta, dtype, split, out_bf16, seq_major))
+        bsz = 2 if rng.random() < 0.25 else 1
+        out.append((i, d, hkv, group, nq, nk, delta, dtype, split, out_bf16, seq_major, bsz))
     return out
 
 
 @pytest.mark.parametrize("case", _fwd_cases(40, 20261203), ids=lambda c: f"fwd{c[0]}")
 def test_fuzz_segment_fwd(case):
-    i, d, hkv, group, nq, nk, delta, dtype, split, out_bf16, seq_major = case
+    i, d, hkv, group, nq, nk, delta, dtype, split, out_bf16, seq_major, bsz = case
     hq = hkv * group
-    q, k, v = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d)], 7000 + i, dtype)
+    q, k, v = draw([(bsz, hq, nq, d), (bsz, hkv, nk, d), (bsz, hkv, nk, d)], 7000 + i, dtype)
     o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v),
                                    delta=oracle.NONCAUSAL if delta is None else delta)
     qd, kd, vd = (_dev(t, seq_major) for t in (q, k, v))
@@ -87,16 +89,17 @@ def _bwd_cases(count, seed):
         delta = None if rng.random() < 0.25 else int(rng.integers(-nq - 20, nk + 20))
         grads_bf16 = bool(rng.random() < 0.3)
         seq_major = bool(rng.random() < 0.3)
-        out.append((i, d, hkv, group, nq, nk, delta, grads_bf16, seq_major))
+        bsz = 2 if rng.random() < 0.25 else 1
+        out.append((i, d, hkv, group, nq, nk, delta, grads_bf16, seq_major, bsz))
     return out
 
 
 @pytest.mark.parametrize("case", _bwd_cases(20, 20261204), ids=lambda c: f"bwd{c[0]}")
 def test_fuzz_segment_bwd(case):
-    i, d, hkv, group, nq, nk, delta, grads_bf16, seq_major = case
+    i, d, hkv, group, nq, nk, delta, grads_bf16, seq_major, bsz = case
     hq = hkv * group
-    q, k, v, do = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d), (1, hq, nq, d)],
-                       7500 + i)
+    q, k, v, do = draw([(bsz, hq, nq, d), (bsz, hkv, nk, d), (bsz, hkv, nk, d),
+                        (bsz, hq, nq, d)], 7500 + i)
     dl = oracle.NONCAUSAL if delta is None else delta
     ref = oracle.attn_bwd(_np32(q), _np32(k), _np32(v), _np32(do), delta=dl)
     qd, kd, vd, dod = (_dev(t, seq_major) for t in (q, k, v, do))
@@ -123,15 +126,17 @@ def _dilated_cases(count, seed):
         rs = [int(rng.integers(1, 13)) for _ in range(nb)]
         causal = bool(rng.random() < 0.5)
         head_shift = bool(rng.random() < 0.4)
-        out.append((i, d, hkv, group, n, tuple(ws), tuple(rs), causal, head_shift))
+        bsz = 2 if rng.random() < 0.25 else 1
+        out.append((i, d, hkv, group, n, tuple(ws), tuple(rs), causal, head_shift, bsz))
     return out
 
 
 @pytest.mark.parametrize("case", _dilated_cases(16, 20261205), ids=lambda c: f"dil{c[0]}")
 def test_fuzz_dilated(case):
-    i, d, hkv, group, n, ws, rs, causal, head_shift = case
+    i, d, hkv, group, n, ws, rs, causal, head_shift, bsz = case
     hq = hkv * group
-    q, k, v, do = draw([(1, hq, n, d), (1, hkv, n, d), (1, hkv, n, d), (1, hq, n, d)], 7800 + i)
+    q, k, v, do = draw([(bsz, hq, n, d), (bsz, hkv, n, d), (bsz, hkv, n, d), (bsz, hq, n, d)],
+                       7800 + i)
     q32, k32, v32, do32 = (_np32(t) for t in (q, k, v, do))
     o_ref, l_ref = oracle.dilated_fwd(q32, k32, v32, ws, rs, causal=causal, head_shift=head_shift)
     ref = oracle.dilated_bwd(q32, k32, v32, do32, ws, rs, causal=causal, head_shift=head_shift)
