@@ -192,8 +192,11 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const int gg = lane >> 4, ip = lane & 15;
 
     const int nkt = (p.Nk + kBKV - 1) / kBKV;
-    const int kt = (int)(blockIdx.x % nkt);
-    const int bsg = (int)(blockIdx.x / nkt);
+    const WorkItem wi = work_item(blockIdx.x, nkt, p.B * p.S * p.Hkv, p.grouped_kv);
+    if (wi.grp >= p.B * p.S * p.Hkv)
+        return;  // padding item of a grouped launch
+    const int kt = wi.t;  // first key tiles see the most query rows
+    const int bsg = wi.grp;
     const int g = bsg % p.Hkv, bs = bsg / p.Hkv;
     const int s = bs % p.S, b = bs / p.S;
     const int k0 = kt * kBKV;
@@ -474,8 +477,11 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
 
     const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
     const int BH = p.B * p.S * p.Hq;
-    const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // longest first
-    const int bsh = (int)(blockIdx.x % BH);
+    const WorkItem wi = work_item(blockIdx.x, nqt, BH, p.grouped_q);
+    if (wi.grp >= BH)
+        return;  // padding item of a grouped launch
+    const int qt = nqt - 1 - wi.t;  // longest first
+    const int bsh = wi.grp;
     const int h = bsh % p.Hq, bs = bsh / p.Hq;
     const int s = bs % p.S, b = bs / p.S;
     const int g = (int)(((int64_t)h * p.Hkv) / p.Hq);
@@ -685,10 +691,13 @@ hipError_t launch_zero_f32(const View &x, int B, int H, int N, int d, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st)
+hipError_t launch_bwd_bf16(const BwdParams &p0, hipStream_t st)
 {
+    BwdParams p = p0;
     const int nkt = (p.Nk + kBKV - 1) / kBKV;
-    const int64_t grid = (int64_t)nkt * p.B * p.S * p.Hkv;
+    const int BSG = p.B * p.S * p.Hkv;
+    p.grouped_kv = use_grouped(nkt, BSG);
+    const int64_t grid = (int64_t)nkt * BSG == 0 ? 0 : work_items(nkt, BSG, p.grouped_kv);
     if (grid > 0) {
         if (p.d == 128)
             hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
@@ -698,9 +707,12 @@ hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t st)
         if (e != hipSuccess)
             return e;
     }
-    const int64_t qgrid = (int64_t)((p.Nq + kQBQ - 1) / kQBQ) * p.B * p.S * p.Hq;
-    if (qgrid == 0 || p.Nk == 0)
+    const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
+    const int BH = p.B * p.S * p.Hq;
+    if ((int64_t)nqt * BH == 0 || p.Nk == 0)
         return hipSuccess;
+    p.grouped_q = use_grouped(nqt, BH);
+    const int64_t qgrid = work_items(nqt, BH, p.grouped_q);
     if (p.d == 128)
         hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
     else

@@ -34,10 +34,12 @@
 //     the accumulator's row interleave;
 //   * causal tiles above the diagonal are never visited; only tiles that
 //     straddle it (or the segment tail) are masked;
-//   * workgroups are issued longest-first (last query tile first) with the
-//     (batch, segment, head) index fastest, so consecutive workgroups -- which
-//     the dispatcher spreads round-robin over the 8 XCDs -- stream the same
-//     K/V tiles at about the same time.
+//   * workgroups are issued longest-first (last query tile first).  With few
+//     (batch, segment, head) groups of many query tiles the group index is
+//     fastest, so consecutive workgroups -- which the dispatcher spreads
+//     round-robin over the 8 XCDs -- stream the same K/V tiles at about the
+//     same time; with many groups of at most 32 query tiles each group's
+//     tiles run together on one XCD and share its L2 (work_item).
 #include "common.h"
 
 namespace seqattn {
@@ -143,8 +145,11 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 
     const int nqt = (p.Nq + kBQ - 1) / kBQ;
     const int BH = p.B * p.S * p.Hq;
-    const int qt = nqt - 1 - (int)(blockIdx.x / BH);
-    const int bh = (int)(blockIdx.x % BH);
+    const WorkItem wi = work_item(blockIdx.x, nqt, BH, p.grouped);
+    if (wi.grp >= BH)
+        return;  // padding item of a grouped launch
+    const int qt = nqt - 1 - wi.t;
+    const int bh = wi.grp;
     const int h = bh % p.Hq;
     const int bs = bh / p.Hq;
     const int s = bs % p.S, b = bs / p.S;
@@ -405,12 +410,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t st)
+hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
 {
+    FwdParams p = p0;
     const int nqt = (p.Nq + kBQ - 1) / kBQ;
-    const int64_t grid = (int64_t)nqt * p.B * p.S * p.Hq;
-    if (grid == 0)
+    const int BH = p.B * p.S * p.Hq;
+    if ((int64_t)nqt * BH == 0)
         return hipSuccess;
+    p.grouped = use_grouped(nqt, BH);
+    const int64_t grid = work_items(nqt, BH, p.grouped);
     if (d == 128)
         hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     else
