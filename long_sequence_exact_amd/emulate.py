@@ -99,7 +99,7 @@ def _blocks(t, P, blk, first_block, count):
 
 
 def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True,
-             lanes: int = 2):
+             lanes: int = 1):
     """All P ranks of a ring, run one after another on one GPU.
 
     q, k, v: [B,H,N,d]; rank r owns rows [r*N/P, (r+1)*N/P).  Returns the
@@ -112,7 +112,9 @@ def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = T
     With lanes > 1 the ranks are split by r % lanes, each class running its
     steps as such batches on a stream of its own: the classes' launches
     overlap, so one launch's epilogues (the fused merges) run while another
-    computes.  batched=False issues one launch per (rank, step).
+    computes (one stream measures fastest for the causal 16K ring, whose
+    launches use the XCD-grouped work order).  batched=False issues one
+    launch per (rank, step).
     """
     B, H, n, d = q.shape
     blk = n // P
@@ -190,7 +192,7 @@ def zigzag_plan(n: int, P: int):
     return plan
 
 
-def zigzag_ring_fwd(q, k, v, P: int, scale=None, out=None, lse=None, lanes: int = 4):
+def zigzag_ring_fwd(q, k, v, P: int, scale=None, out=None, lse=None, lanes: int = 2):
     """Causal ring over P ranks with the zigzag split, all ranks on one GPU.
 
     q, k, v: [1,H,N,d] in the zigzag layout (zigzag_order; rank r owns rows
