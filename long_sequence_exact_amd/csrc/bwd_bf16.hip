@@ -10,9 +10,9 @@
 //
 // Work decomposition (three launches)
 //   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row);
-//   * bwd_main (dK, dV): one workgroup = 8 waves for 128 keys of one (batch,
-//     KV head): waves 0-3 accumulate dV^T and waves 4-7 dK^T for the same
-//     4 x 32 keys (one fp32 accumulator per wave keeps two waves per SIMD;
+//   * bwd_main (dK, dV, d = 128): one workgroup = 8 waves for 128 keys of one
+//     (batch, KV head): waves 0-3 accumulate dV^T and waves 4-7 dK^T for the
+//     same 4 x 32 keys (one fp32 accumulator per wave keeps two waves per SIMD;
 //     S is computed by both), looping over the query heads sharing the KV
 //     head and over the visible 64-row query tiles; the next tile's Q, dO
 //     rows, LSE and D are loaded into VGPRs (range-checked buffer loads)
@@ -22,6 +22,9 @@
 //     dV^T += dO^T P and dK^T += Q^T dS; the Q^T and dO^T A operands are read
 //     from the row-major Q / dO tiles in LDS with transposing reads
 //     (ds_read_b64_tr_b16);
+//   * bwd_kv64 (dK, dV, d = 64): the same with 8 x 32 keys per workgroup and
+//     both accumulators in each wave, which fit at d = 64, so S and P are
+//     formed once per pair;
 //   * bwd_dq (dQ): query-tile major, shaped like the forward kernel (below).
 //     Recomputing S and dP there costs two more contractions than sharing
 //     them with bwd_main, but dQ then needs no atomics and no round trip of
@@ -114,9 +117,7 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(View x, int B, int H, int
 
 template <int D>
 struct BCfg {
-    // query rows per iteration: 128 at d = 64, where one step's contractions
-    // are half as long, so barriers and staging weigh as much as at d = 128
-    static constexpr int BQ = D == 64 ? 2 * kBQ : kBQ;
+    static constexpr int BQ = kBQ;  // query rows per iteration
     static constexpr int CPT = BQ * D / 8 / kThreads;  // 16-byte chunks per thread per tile
     static_assert(CPT * kThreads * 8 == BQ * D, "tile split");
 };
@@ -443,6 +444,263 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
+// dK and dV at d = 64 in one wave: one workgroup = 8 waves = 256 keys of one
+// (batch, KV head), wave = 32 keys holding both accumulators (dV^T and
+// dK^T / sigma, 2 x 32 VGPRs at d = 64), so S and P are formed once per
+// (query, key) pair instead of once per wave of a dV/dK pair.  Staging and
+// operand layouts as in bwd_main_kernel.
+// ---------------------------------------------------------------------------
+
+template <int D, int BQ, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_kv_kernel(const BwdParams p)
+{
+    constexpr int kThreads = 64 * NW, kFKeys = 32 * NW;
+    constexpr int CPT = BQ * D / 8 / kThreads;
+    static_assert(CPT * kThreads * 8 == BQ * D, "tile split");
+    __shared__ __attribute__((aligned(16))) char Qs[BQ * 2 * D];
+    __shared__ __attribute__((aligned(16))) char dOs[BQ * 2 * D];
+    __shared__ float lse2s[BQ];
+    __shared__ float Dsh[BQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int gg = lane >> 4, ip = lane & 15;
+
+    const int nkt = (p.Nk + kFKeys - 1) / kFKeys;
+    const WorkItem wi = work_item(blockIdx.x, nkt, p.B * p.S * p.Hkv, p.grouped_kv);
+    if (wi.grp >= p.B * p.S * p.Hkv)
+        return;  // padding item of a grouped launch
+    const int kt = wi.t;
+    const int bsg = wi.grp;
+    const int g = bsg % p.Hkv, bs = bsg / p.Hkv;
+    const int s = bs % p.S, b = bs / p.S;
+    const int k0 = kt * kFKeys;
+    const int kw0 = k0 + wave * 32;
+    const int key = kw0 + l32;
+    const HeadRows hr = head_rows(p.hs_r, p.hs_len, p.Nk, g);
+    const int Nk = hr.n, Nq = p.hs_r > 0 ? hr.n : p.Nq;
+    if (k0 >= Nk)
+        return;
+
+    const bf16 *K = (const bf16 *)p.k.ptr + b * p.k.sb + s * p.k.ss + g * p.k.sh +
+                    head_shift_elems(p.k, p.hs_r, hr.off);
+    const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh +
+                    head_shift_elems(p.v, p.hs_r, hr.off);
+    const int64_t sq = head_shift_elems(p.q, p.hs_r, hr.off);
+    const int64_t so = head_shift_elems(p.dout, p.hs_r, hr.off);
+    const int64_t sl = head_shift_elems(p.lse, p.hs_r, hr.off);
+    const int64_t sd = head_shift_elems(p.dvec, p.hs_r, hr.off);
+
+    bf16x8 kB[D / 16], vB[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        if (key < Nk) {
+            xk = *(const u32x4 *)(K + (int64_t)key * p.k.sn + kk * 16 + hl * 8);
+            xv = *(const u32x4 *)(V + (int64_t)key * p.v.sn + kk * 16 + hl * 8);
+        }
+        kB[kk] = __builtin_bit_cast(bf16x8, xk);
+        vB[kk] = __builtin_bit_cast(bf16x8, xv);
+    }
+
+    f32x16 accV[D / 32], accK[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            accV[i][e] = accK[i][e] = 0.f;
+
+    const float c = p.scale * kLog2e;
+    const int group = p.Hq / p.Hkv;
+    const int nqt = (Nq + BQ - 1) / BQ;
+    int qt_begin = 0;
+    if (!p.noncausal) {
+        const int first_q = max(0, k0 - p.delta);
+        qt_begin = min(nqt, first_q / BQ);
+    }
+    const int per_head = nqt - qt_begin;
+    const int niters = group * per_head;
+
+    u32x4 qreg[CPT], oreg[CPT];
+    float lreg = 0.f, dreg = 0.f;
+    int srow[CPT], scol[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = tid + u * kThreads;
+        srow[u] = ch / (D / 8);
+        scol[u] = (ch % (D / 8)) * 8;
+    }
+    auto prefetch = [&](int it) {
+        const int h = g * group + it / per_head;
+        const int q0 = (qt_begin + it % per_head) * BQ;
+        const bf16 *Q = (const bf16 *)p.q.ptr + b * p.q.sb + s * p.q.ss + h * p.q.sh + sq;
+        const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss +
+                         h * p.dout.sh + so;
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(Nq - 1) * p.q.sn + D) * 2);
+        const __amdgpu_buffer_rsrc_t orr = make_rsrc(dO, ((int64_t)(Nq - 1) * p.dout.sn + D) * 2);
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            qreg[u] = load16(qr, ((q0 + srow[u]) * (int)p.q.sn + scol[u]) * 2);
+            oreg[u] = load16(orr, ((q0 + srow[u]) * (int)p.dout.sn + scol[u]) * 2);
+        }
+        if (tid < BQ) {
+            const int i = q0 + tid;
+            lreg = INFINITY;
+            dreg = 0.f;
+            if (i < Nq) {
+                const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
+                                   h * p.lse.sh + sl + (int64_t)i * p.lse.sn);
+                if (lv != -INFINITY)
+                    lreg = lv * kLog2e;
+                dreg = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss +
+                         h * p.dvec.sh + sd + (int64_t)i * p.dvec.sn);
+            }
+        }
+    };
+
+    const int trow = 4 * (gg >> 1) + (ip >> 2);
+
+    if (niters > 0)
+        prefetch(0);
+
+    for (int it = 0; it < niters; ++it) {
+        const int q0 = (qt_begin + it % per_head) * BQ;
+
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            *(u32x4 *)(Qs + swz_off<D>(srow[u], scol[u] >> 3)) = qreg[u];
+            *(u32x4 *)(dOs + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
+        }
+        if (tid < BQ) {
+            lse2s[tid] = lreg;
+            Dsh[tid] = dreg;
+        }
+        __syncthreads();
+        if (it + 1 < niters)
+            prefetch(it + 1);
+
+        // this wave's keys all in the future of the whole query tile: nothing
+        if (!p.noncausal && kw0 > q0 + BQ - 1 + p.delta)
+            continue;
+        const bool need_mask = (kw0 + 32 > Nk) || (q0 + BQ > Nq) ||
+                               (!p.noncausal && kw0 + 31 > q0 + p.delta);
+        unsigned pB[BQ / 32][8], dB[BQ / 32][8];  // P and dS, bf16 pairs
+#pragma unroll
+        for (int qb = 0; qb < BQ / 32; ++qb) {
+            f32x16 sv, dp;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                sv[e] = dp[e] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const int off = swz_off<D>(qb * 32 + l32, 2 * kk + hl);
+                const bf16x8 aq = *(const bf16x8 *)(Qs + off);
+                const bf16x8 ad = *(const bf16x8 *)(dOs + off);
+                sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], sv, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int u = 0; u < 2 * (D / 16) - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int r0 = qb * 32 + gq * 8 + hl * 4;
+                const float4 l2 = *(const float4 *)(&lse2s[r0]);
+                const float4 dd = *(const float4 *)(&Dsh[r0]);
+                const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+                const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
+                float pv[4], dsv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = gq * 4 + u;
+                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -lv[u]));
+                    if (need_mask) {
+                        const int qi = q0 + r0 + u;
+                        const bool vis = key < Nk && qi < Nq &&
+                                         (p.noncausal || key - qi <= p.delta);
+                        pe = vis ? pe : 0.f;
+                    }
+                    pv[u] = pe;
+                    dsv[u] = pe * (dp[e] - dv[u]);
+                }
+                pB[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
+                pB[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
+                dB[qb][gq * 2 + 0] = pack_bf16(dsv[0], dsv[1]);
+                dB[qb][gq * 2 + 1] = pack_bf16(dsv[2], dsv[3]);
+            }
+        }
+
+        // dV^T += dO^T P and dK^T += Q^T dS (k = the tile's BQ query rows)
+#pragma unroll
+        for (int ks = 0; ks < BQ / 16; ++ks) {
+            const int qb = ks >> 1, half = ks & 1;
+            u32x4 wp = {pB[qb][half * 4 + 0], pB[qb][half * 4 + 1], pB[qb][half * 4 + 2],
+                        pB[qb][half * 4 + 3]};
+            u32x4 wd = {dB[qb][half * 4 + 0], dB[qb][half * 4 + 1], dB[qb][half * 4 + 2],
+                        dB[qb][half * 4 + 3]};
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, wp);
+            const bf16x8 bd = __builtin_bit_cast(bf16x8, wd);
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const int cc = 4 * i + 2 * (gg & 1) + ((ip & 3) >> 1);
+                const int o0 = swz_off<D>(16 * ks + trow, cc) + (ip & 1) * 8;
+                const int o1 = swz_off<D>(16 * ks + 8 + trow, cc) + (ip & 1) * 8;
+                const bf16x8 ao = cat_tr(read_tr((const bf16 *)(dOs + o0)), read_tr((const bf16 *)(dOs + o1)));
+                const bf16x8 aq = cat_tr(read_tr((const bf16 *)(Qs + o0)), read_tr((const bf16 *)(Qs + o1)));
+                accV[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bp, accV[i], 0, 0, 0);
+                accK[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bd, accK[i], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < 2 * (BQ / 16) * (D / 32) - 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+
+    if (key >= Nk)
+        return;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const View &out = which ? p.dk : p.dv;
+        const int out_f32 = which ? p.dk_f32 : p.dv_f32;
+        const float f = which ? p.scale : 1.f;
+        const int64_t krow = b * out.sb + s * out.ss + g * out.sh +
+                             head_shift_elems(out, p.hs_r, hr.off) + (int64_t)key * out.sn;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = i * 32 + gq * 8 + hl * 4;
+                const f32x16 &a = which ? accK[i] : accV[i];
+                const float x0 = a[gq * 4 + 0] * f, x1 = a[gq * 4 + 1] * f;
+                const float x2 = a[gq * 4 + 2] * f, x3 = a[gq * 4 + 3] * f;
+                if (p.acc_kv) {
+                    float4 *dst = (float4 *)((float *)out.ptr + krow + d0);
+                    float4 w = *dst;
+                    w.x += x0; w.y += x1; w.z += x2; w.w += x3;
+                    *dst = w;
+                } else if (out_f32) {
+                    float4 w = {x0, x1, x2, x3};
+                    *(float4 *)((float *)out.ptr + krow + d0) = w;
+                } else {
+                    uint2 w = {pack_bf16(x0, x1), pack_bf16(x2, x3)};
+                    *(uint2 *)((bf16 *)out.ptr + krow + d0) = w;
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ, query-tile major: one workgroup = 8 waves = 256 query rows of one
 // (batch, query head); wave = 32 rows, whose Q and dO rows are the B operands
 // (VGPRs) of S^T = K Q^T and dP^T = V dO^T.  With queries in lane columns, a
@@ -694,7 +952,8 @@ hipError_t launch_zero_f32(const View &x, int B, int H, int N, int d, hipStream_
 hipError_t launch_bwd_bf16(const BwdParams &p0, hipStream_t st)
 {
     BwdParams p = p0;
-    const int nkt = (p.Nk + kBKV - 1) / kBKV;
+    const int keys = p.d == 128 ? kBKV : 256;
+    const int nkt = (p.Nk + keys - 1) / keys;
     const int BSG = p.B * p.S * p.Hkv;
     p.grouped_kv = use_grouped(nkt, BSG);
     const int64_t grid = (int64_t)nkt * BSG == 0 ? 0 : work_items(nkt, BSG, p.grouped_kv);
@@ -702,7 +961,7 @@ hipError_t launch_bwd_bf16(const BwdParams &p0, hipStream_t st)
         if (p.d == 128)
             hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
         else
-            hipLaunchKernelGGL(bwd_main_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+            hipLaunchKernelGGL((bwd_kv_kernel<64, kBQ, 8>), dim3((unsigned)grid), dim3(512), 0, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
