@@ -12,15 +12,18 @@
 //   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row);
 //   * bwd_main (dK, dV, d = 128): one workgroup = 8 waves for 128 keys of one
 //     (batch, KV head): waves 0-3 accumulate dV^T and waves 4-7 dK^T for the
-//     same 4 x 32 keys (one fp32 accumulator per wave keeps two waves per SIMD;
-//     S is computed by both), looping over the query heads sharing the KV
-//     head and over the visible 64-row query tiles; the next tile's Q, dO
-//     rows, LSE and D are loaded into VGPRs (range-checked buffer loads)
-//     while the current tile is computed.  Per tile the scores are
-//     recomputed as S = Q K^T with keys in lane columns
-//     (v_mfma_f32_32x32x16_bf16), so P and dS are directly the B operands of
-//     dV^T += dO^T P and dK^T += Q^T dS; the Q^T and dO^T A operands are read
-//     from the row-major Q / dO tiles in LDS with transposing reads
+//     same 4 x 32 keys (one fp32 accumulator per wave keeps two waves per
+//     SIMD), looping over the query heads sharing the KV head and over the
+//     visible 64-row query tiles.  Per tile the dV wave recomputes
+//     S = Q K^T with keys in lane columns (v_mfma_f32_32x32x16_bf16) and
+//     P, so P is directly the B operand of dV^T += dO^T P, and hands P
+//     (bf16) through LDS to the dK wave of its pair, which takes the tile
+//     one step later: dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS.  The
+//     lag lets one barrier per step order both the hand-over and the Q / dO
+//     tiles, which sit in three LDS buffers (the dV waves' tile, the dK
+//     waves' tile and the next one, stored from VGPRs loaded a step ahead
+//     with range-checked buffer loads).  The Q^T and dO^T A operands are
+//     read from the row-major tiles with transposing reads
 //     (ds_read_b64_tr_b16);
 //   * bwd_kv64 (dK, dV, d = 64): the same with 8 x 32 keys per workgroup and
 //     both accumulators in each wave, which fit at d = 64, so S and P are
@@ -178,17 +181,24 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 {
     using C = BCfg<D>;
     constexpr int BQ = C::BQ;
-    __shared__ __attribute__((aligned(16))) char Qs[BQ * 2 * D];
-    __shared__ __attribute__((aligned(16))) char dOs[BQ * 2 * D];
-    __shared__ float lse2s[BQ];
-    __shared__ float Dsh[BQ];
+    constexpr int TB = BQ * 2 * D;           // bytes of one Q or dO tile
+    constexpr int PB = (BQ / 32) * 64 * 32;  // bytes of one wave pair's P tile
+    // Q / dO tiles in three buffers: the dV waves read tile it, the dK waves
+    // tile it - 1, and tile it + 1 is stored meanwhile
+    __shared__ __attribute__((aligned(16))) char Qs[3 * TB];
+    __shared__ __attribute__((aligned(16))) char dOs[3 * TB];
+    // P of each wave pair, written by its dV wave, read one step later by
+    // its dK wave (double-buffered), in the accumulator's lane layout (per
+    // 32-query block: lane l's first 16 bytes at 16 l, its last 16 at 1024 + 16 l)
+    __shared__ __attribute__((aligned(16))) char Ps[2 * 4 * PB];
+    __shared__ float lse2s[3][BQ];
+    __shared__ float Dsh[3][BQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // waves 0-3 form dV, waves 4-7 form dK, for the same 4 x 32 keys: every
-    // wave holds one fp32 accumulator and two waves share each SIMD
     const bool is_dk = wave >= 4;
+    const int pair = wave & 3;
     const int l32 = lane & 31, hl = lane >> 5;
     const int gg = lane >> 4, ip = lane & 15;
 
@@ -201,10 +211,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const int g = bsg % p.Hkv, bs = bsg / p.Hkv;
     const int s = bs % p.S, b = bs / p.S;
     const int k0 = kt * kBKV;
-    const int kw0 = k0 + (wave & 3) * 32;
+    const int kw0 = k0 + pair * 32;
     const int key = kw0 + l32;  // this lane's key (accumulator column)
-    // rows of this head (fewer, and shifted, under head-dependent offsets,
-    // where the KV head has exactly one query head)
     const HeadRows hr = head_rows(p.hs_r, p.hs_len, p.Nk, g);
     const int Nk = hr.n, Nq = p.hs_r > 0 ? hr.n : p.Nq;
     if (k0 >= Nk)
@@ -214,26 +222,24 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                     head_shift_elems(p.k, p.hs_r, hr.off);
     const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh +
                     head_shift_elems(p.v, p.hs_r, hr.off);
-    // the same shift of the query-side views (all query heads of this
-    // workgroup share it)
     const int64_t sq = head_shift_elems(p.q, p.hs_r, hr.off);
     const int64_t so = head_shift_elems(p.dout, p.hs_r, hr.off);
     const int64_t sl = head_shift_elems(p.lse, p.hs_r, hr.off);
     const int64_t sd = head_shift_elems(p.dvec, p.hs_r, hr.off);
 
-    // the wave's K rows (and, for dK, V rows) as B operands (k = d): lane
-    // holds key `key`, d = 16kk + 8hl .. +8
-    bf16x8 kB[D / 16], vB[D / 16];
+    // B operands (k = d): K rows for the dV waves' S, V rows for the dK
+    // waves' dP; lane holds key `key`, d = 16kk + 8hl .. +8
+    bf16x8 rB[D / 16];
+    {
+        const bf16 *R = is_dk ? V : K;
+        const int64_t rs = is_dk ? p.v.sn : p.k.sn;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-        if (key < Nk) {
-            xk = *(const u32x4 *)(K + (int64_t)key * p.k.sn + kk * 16 + hl * 8);
-            if (is_dk)
-                xv = *(const u32x4 *)(V + (int64_t)key * p.v.sn + kk * 16 + hl * 8);
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (key < Nk)
+                x = *(const u32x4 *)(R + (int64_t)key * rs + kk * 16 + hl * 8);
+            rB[kk] = __builtin_bit_cast(bf16x8, x);
         }
-        kB[kk] = __builtin_bit_cast(bf16x8, xk);
-        vB[kk] = __builtin_bit_cast(bf16x8, xv);
     }
 
     f32x16 acc[D / 32];  // dV^T (waves 0-3) or dK^T / sigma (waves 4-7)
@@ -254,7 +260,6 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const int per_head = nqt - qt_begin;
     const int niters = group * per_head;
 
-    // staging of the (query head, query tile) of iteration `it` into VGPRs
     u32x4 qreg[C::CPT], oreg[C::CPT];
     float lreg = 0.f, dreg = 0.f;
     int srow[C::CPT], scol[C::CPT];
@@ -291,62 +296,60 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             }
         }
     };
-
-    // transposing-read offset (see read_tr) of the Q^T / dO^T operands, in the
-    // query order of the P / dS accumulator rows
-    // (row 4 (gg/2) + ip/4 + 8 rr + 16 ks, chunk 4 i + 2 (gg%2) + (ip%4)/2,
-    // 8-byte half ip%2)
-    const int trow = 4 * (gg >> 1) + (ip >> 2);
-    const char *At = is_dk ? Qs : dOs;  // A operand of dK^T += Q^T dS / dV^T += dO^T P
-
-    if (niters > 0)
-        prefetch(0);
-
-    for (int it = 0; it < niters; ++it) {
-        const int q0 = (qt_begin + it % per_head) * BQ;
-
-        __syncthreads();  // previous iteration done with Qs, dOs
+    auto stage = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < C::CPT; ++u) {
-            *(u32x4 *)(Qs + swz_off<D>(srow[u], scol[u] >> 3)) = qreg[u];
-            *(u32x4 *)(dOs + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
+            *(u32x4 *)(Qs + buf * TB + swz_off<D>(srow[u], scol[u] >> 3)) = qreg[u];
+            *(u32x4 *)(dOs + buf * TB + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
         }
         if (tid < BQ) {
-            lse2s[tid] = lreg;
-            Dsh[tid] = dreg;
+            lse2s[buf][tid] = lreg;
+            Dsh[buf][tid] = dreg;
         }
-        __syncthreads();
-        if (it + 1 < niters)
-            prefetch(it + 1);
+    };
 
-        // ---- S = Q K^T (and dP = dO V^T for dK) for BQ / 32 blocks of 32 queries ----
-        const bool need_mask = (k0 + kBKV > Nk) || (q0 + BQ > Nq) ||
-                               (!p.noncausal && k0 + kBKV - 1 > q0 + p.delta);
+    const int trow = 4 * (gg >> 1) + (ip >> 2);
+
+    if (niters > 0) {
+        prefetch(0);
+        stage(0);
+        if (niters > 1)
+            prefetch(1);
+    }
+
+    // step it: the dV waves take tile it, the dK waves tile it - 1
+    for (int it = 0; it <= niters && niters > 0; ++it) {
+        // tile it staged, P(it - 1) written, and buffer (it + 1) % 3 (tile
+        // it - 2) no longer read
+        __syncthreads();
+        if (it + 1 < niters) {
+            stage((it + 1) % 3);
+            if (it + 2 < niters)
+                prefetch(it + 2);
+        }
+        const int tq = is_dk ? it - 1 : it;  // this wave's tile
+        if (tq < 0 || tq >= niters)
+            continue;
+        const int buf = tq % 3;
+        const char *Qb = Qs + buf * TB;
+        const char *Ob = dOs + buf * TB;
+        char *Pp = Ps + ((tq & 1) * 4 + pair) * PB + lane * 16;
+        const int q0 = (qt_begin + tq % per_head) * BQ;
+
         unsigned pB[BQ / 32][8];  // P (dV waves) or dS (dK waves), bf16 pairs
+        if (!is_dk) {
+            const bool need_mask = (kw0 + 32 > Nk) || (q0 + BQ > Nq) ||
+                                   (!p.noncausal && kw0 + 31 > q0 + p.delta);
 #pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb) {
-            f32x16 s, dp;
+            for (int qb = 0; qb < BQ / 32; ++qb) {
+                f32x16 sv;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                s[e] = dp[e] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 aq = *(const bf16x8 *)(Qs + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], s, 0, 0, 0);
-            }
-            // keep four operand reads in flight ahead of the MFMA that uses them
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int u = 0; u < D / 16 - 4; ++u) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            if (is_dk) {
+                for (int e = 0; e < 16; ++e)
+                    sv[e] = 0.f;
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
-                    const bf16x8 ad = *(const bf16x8 *)(dOs + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
+                    const bf16x8 aq = *(const bf16x8 *)(Qb + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
+                    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, rB[kk], sv, 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -355,39 +358,70 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            }
-            // element e: query row qb*32 + 8(e/4) + 4hl + e%4 of the tile
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int r0 = qb * 32 + gq * 8 + hl * 4;
-                const float4 l2 = *(const float4 *)(&lse2s[r0]);
-                const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-                float pv[4];
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int r0 = qb * 32 + gq * 8 + hl * 4;
+                    const float4 l2 = *(const float4 *)(&lse2s[buf][r0]);
+                    const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+                    float pv[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = gq * 4 + u;
-                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -lv[u]));
-                    if (need_mask) {
-                        const int qi = q0 + r0 + u;
-                        const bool vis = key < Nk && qi < Nq &&
-                                         (p.noncausal || key - qi <= p.delta);
-                        pe = vis ? pe : 0.f;
+                    for (int u = 0; u < 4; ++u) {
+                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gq * 4 + u], c, -lv[u]));
+                        if (need_mask) {
+                            const int qi = q0 + r0 + u;
+                            const bool vis = key < Nk && qi < Nq &&
+                                             (p.noncausal || key - qi <= p.delta);
+                            pe = vis ? pe : 0.f;
+                        }
+                        pv[u] = pe;
                     }
-                    pv[u] = pe;
+                    pB[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
+                    pB[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
                 }
-                if (is_dk) {
-                    const float4 dd = *(const float4 *)(&Dsh[r0]);
-                    pv[0] *= dp[gq * 4 + 0] - dd.x;
-                    pv[1] *= dp[gq * 4 + 1] - dd.y;
-                    pv[2] *= dp[gq * 4 + 2] - dd.z;
-                    pv[3] *= dp[gq * 4 + 3] - dd.w;
+                // hand P to the dK wave of the pair (read next step)
+                *(u32x4 *)(Pp + qb * 2048) = u32x4{pB[qb][0], pB[qb][1], pB[qb][2], pB[qb][3]};
+                *(u32x4 *)(Pp + qb * 2048 + 1024) = u32x4{pB[qb][4], pB[qb][5], pB[qb][6], pB[qb][7]};
+            }
+        } else {
+#pragma unroll
+            for (int qb = 0; qb < BQ / 32; ++qb) {
+                f32x16 dp;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    dp[e] = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const bf16x8 ad = *(const bf16x8 *)(Ob + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, rB[kk], dp, 0, 0, 0);
                 }
-                pB[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
-                pB[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int u = 0; u < D / 16 - 4; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                // P from the dV wave (zero where masked), dS = P o (dP - D)
+                const u32x4 w0 = *(const u32x4 *)(Pp + qb * 2048);
+                const u32x4 w1 = *(const u32x4 *)(Pp + qb * 2048 + 1024);
+                const unsigned pw[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int r0 = qb * 32 + gq * 8 + hl * 4;
+                    const float4 dd = *(const float4 *)(&Dsh[buf][r0]);
+                    const unsigned a0 = pw[gq * 2 + 0], a1 = pw[gq * 2 + 1];
+                    const float d0 = bf16_lo(a0) * (dp[gq * 4 + 0] - dd.x);
+                    const float d1 = bf16_hi(a0) * (dp[gq * 4 + 1] - dd.y);
+                    const float d2 = bf16_lo(a1) * (dp[gq * 4 + 2] - dd.z);
+                    const float d3 = bf16_hi(a1) * (dp[gq * 4 + 3] - dd.w);
+                    pB[qb][gq * 2 + 0] = pack_bf16(d0, d1);
+                    pB[qb][gq * 2 + 1] = pack_bf16(d2, d3);
+                }
             }
         }
 
         // ---- dV^T += dO^T P or dK^T += Q^T dS (k = the tile's BQ query rows) ----
+        const char *At = is_dk ? Qb : Ob;
 #pragma unroll
         for (int ks = 0; ks < BQ / 16; ++ks) {
             const int qb = ks >> 1, half = ks & 1;
@@ -396,14 +430,13 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             const bf16x8 bb = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const int c = 4 * i + 2 * (gg & 1) + ((ip & 3) >> 1);
-                const int o0 = swz_off<D>(16 * ks + trow, c) + (ip & 1) * 8;
-                const int o1 = swz_off<D>(16 * ks + 8 + trow, c) + (ip & 1) * 8;
+                const int cc = 4 * i + 2 * (gg & 1) + ((ip & 3) >> 1);
+                const int o0 = swz_off<D>(16 * ks + trow, cc) + (ip & 1) * 8;
+                const int o1 = swz_off<D>(16 * ks + 8 + trow, cc) + (ip & 1) * 8;
                 const bf16x8 a = cat_tr(read_tr((const bf16 *)(At + o0)), read_tr((const bf16 *)(At + o1)));
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[i], 0, 0, 0);
             }
         }
-        // two transposing reads per MFMA; keep four MFMAs' worth in flight
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
         for (int u = 0; u < (BQ / 16) * (D / 32) - 4; ++u) {
