@@ -61,25 +61,27 @@ __device__ inline unsigned pack_bf16(float a, float b)
 __device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// D_i = sum_c dO_ic O_ic; 16 lanes per row, d/16 elements per lane.
+// D_i = sum_c dO_ic O_ic; 16 lanes per row, d/16 elements per lane, rows
+// strided over the grid.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
 {
     const int64_t rows = (int64_t)p.B * p.S * p.Hq * p.Nq;
-    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
+    const int64_t step = (int64_t)gridDim.x * (256 / 16);
     const int sub = threadIdx.x & 15;
     const int per = p.d / 16;  // 4 or 8
-    float acc = 0.f;
-    int i = 0, h = 0, s = 0, b = 0;
-    if (row < rows) {
-        i = (int)(row % p.Nq);
+    // every lane of a 16-lane group runs the same rows, so the shuffle below
+    // always has all 16 partners
+    for (int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16; row < rows; row += step) {
+        const int i = (int)(row % p.Nq);
         int64_t r = row / p.Nq;
-        h = (int)(r % p.Hq);
+        const int h = (int)(r % p.Hq);
         r /= p.Hq;
-        s = (int)(r % p.S);
-        b = (int)(r / p.S);
+        const int s = (int)(r % p.S);
+        const int b = (int)(r / p.S);
         const bf16 *dO = (const bf16 *)p.dout.ptr + b * p.dout.sb + s * p.dout.ss +
                          h * p.dout.sh + (int64_t)i * p.dout.sn + sub * per;
         const int64_t ooff = b * p.o.sb + s * p.o.ss + h * p.o.sh + (int64_t)i * p.o.sn + sub * per;
+        float acc = 0.f;
         for (int c = 0; c < per; c += 4) {
             const uint2 g = *(const uint2 *)(dO + c);
             float o0, o1, o2, o3;
@@ -92,13 +94,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
             }
             acc += bf16_lo(g.x) * o0 + bf16_hi(g.x) * o1 + bf16_lo(g.y) * o2 + bf16_hi(g.y) * o3;
         }
-    }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-        acc += __shfl_xor(acc, m, 16);
-    if (row < rows && sub == 0)
-        *((float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss + h * p.dvec.sh +
-          (int64_t)i * p.dvec.sn) = acc;
+        for (int m = 8; m >= 1; m >>= 1)
+            acc += __shfl_xor(acc, m, 16);
+        if (sub == 0)
+            *((float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss + h * p.dvec.sh +
+              (int64_t)i * p.dvec.sn) = acc;
+    }
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(View x, int B, int H, int N, int d)
@@ -968,7 +970,9 @@ hipError_t launch_bwd_prep(const BwdParams &p, hipStream_t st)
     const int64_t rows = (int64_t)p.B * p.S * p.Hq * p.Nq;
     if (rows == 0)
         return hipSuccess;
-    const int64_t blocks = (rows * 16 + 255) / 256;
+    int64_t blocks = (rows * 16 + 255) / 256;
+    if (blocks > 256 * 64)
+        blocks = 256 * 64;  // rows strided over the grid
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
     return hipGetLastError();
 }
@@ -990,6 +994,8 @@ hipError_t launch_bwd_bf16(const BwdParams &p0, hipStream_t st)
     const int BSG = p.B * p.S * p.Hkv;
     p.grouped_kv = use_grouped(nkt, BSG);
     const int64_t grid = (int64_t)nkt * BSG == 0 ? 0 : work_items(nkt, BSG, p.grouped_kv);
+    if (!grid_fits(grid, kThreads))
+        return hipErrorInvalidConfiguration;
     if (grid > 0) {
         if (p.d == 128)
             hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
@@ -1005,6 +1011,8 @@ hipError_t launch_bwd_bf16(const BwdParams &p0, hipStream_t st)
         return hipSuccess;
     p.grouped_q = use_grouped(nqt, BH);
     const int64_t qgrid = work_items(nqt, BH, p.grouped_q);
+    if (!grid_fits(qgrid, kQThreads))
+        return hipErrorInvalidConfiguration;
     if (p.d == 128)
         hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
     else

@@ -83,6 +83,11 @@ __device__ inline WorkItem work_item(unsigned blk, int ntile, int ngrp, int grou
     const int idx = j - band * bg * ntile;
     return {(band * bg + idx % nb) * kXcds + xcd, idx / nb};
 }
+// A dispatch counts its work-items in 32 bits.
+inline bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks * threads <= (int64_t)0xffffffff;
+}
 inline int use_grouped(int ntile, int ngrp)
 {
     return ngrp >= kXcds && ntile <= kGroupMaxTiles;

@@ -419,6 +419,8 @@ hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
         return hipSuccess;
     p.grouped = use_grouped(nqt, BH);
     const int64_t grid = work_items(nqt, BH, p.grouped);
+    if (!grid_fits(grid, kThreads))
+        return hipErrorInvalidConfiguration;
     if (d == 128)
         hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     else

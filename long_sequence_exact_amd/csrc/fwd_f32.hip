@@ -122,6 +122,8 @@ hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t st)
     const int64_t grid = (int64_t)nqt * p.B * p.S * p.Hq;
     if (grid == 0)
         return hipSuccess;
+    if (!grid_fits(grid, kRows))
+        return hipErrorInvalidConfiguration;
     if (d == 128)
         hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(kRows), 0, st, p);
     else
