@@ -9,7 +9,8 @@
 //   dV = P^T dO,  dS = P o (dO V^T - D),  dK = sigma dS^T Q,  dQ += sigma dS K.
 //
 // Work decomposition (three launches)
-//   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row);
+//   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row, rows
+//     strided over a capped grid);
 //   * bwd_main (dK, dV, d = 128): one workgroup = 8 waves for 128 keys of one
 //     (batch, KV head): waves 0-3 accumulate dV^T and waves 4-7 dK^T for the
 //     same 4 x 32 keys (one fp32 accumulator per wave keeps two waves per
@@ -25,7 +26,7 @@
 //     with range-checked buffer loads).  The Q^T and dO^T A operands are
 //     read from the row-major tiles with transposing reads
 //     (ds_read_b64_tr_b16);
-//   * bwd_kv64 (dK, dV, d = 64): the same with 8 x 32 keys per workgroup and
+//   * bwd_kv (dK, dV, d = 64): the same with 8 x 32 keys per workgroup and
 //     both accumulators in each wave, which fit at d = 64, so S and P are
 //     formed once per pair;
 //   * bwd_dq (dQ): query-tile major, shaped like the forward kernel (below).
