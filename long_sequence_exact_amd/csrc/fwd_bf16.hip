@@ -28,7 +28,9 @@
 //   * the reference max of a row is only raised when new scores exceed it by
 //     more than 2^8 (a conditional rescale): the exponentials stay <= 256,
 //     which fp32 and bf16 hold with full relative precision, and the O
-//     rescale is skipped for most tiles;
+//     rescale is skipped for most tiles; at d = 128 the tile's max is not
+//     even taken unless the exponentials against the current reference sum
+//     to more than 2^16 in some lane (then the tile is redone);
 //   * P^T is rounded to bf16 in registers and is directly the B operand of
 //     O^T += V^T P^T; the transposing reads of V deliver keys in the order of
 //     the accumulator's row interleave;
@@ -56,6 +58,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 headroom before the max is raised
+constexpr float kLazyBound = 65536.f;  // largest lane sum of P kept without a rescale (d = 128)
 constexpr int kBK = 128;              // keys per K/V tile
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
@@ -201,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
 
     float m_run = -INFINITY;  // running reference max, in units of log2
     float l_run = 0.f;        // this lane's partial row sum
+    bool all_ref = false;     // every row of the wave has a finite reference
     const float c = p.scale * kLog2e;
 
     // K/V tiles go HBM -> LDS by direct buffer loads into unpadded rows:
@@ -289,46 +293,102 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
                 }
         }
 
-        float mx = -INFINITY;
+        unsigned pk[BK / 32][8];  // P, bf16 pairs
+        if constexpr (D == 128) {
+            // P = exp2(S c - m) rounded to bf16, and this lane's sum of P
+            auto exps = [&](float m) {
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < BK / 32; ++kb)
+                for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                mx = fmaxf(mx, sacc[kb][e]);
-        mx = lane_pair_max(mx);
+                    for (int e = 0; e < 16; e += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], c, -m));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], c, -m));
+                        pk[kb][e >> 1] = pack_bf16(p0, p1);
+                        s0 += p0;
+                        s1 += p1;
+                    }
+                return s0 + s1;
+            };
 
-        // conditional rescale: raise the reference max only when some score
-        // exceeds it by more than the slack (always on a row's first keys)
-        const float mxc = mx * c;
-        const bool upd = mxc > m_run + kRescaleSlack;
-        const bool any_upd = __any(upd);
-        float alpha = 1.f;
-        if (any_upd) {
-            const float m_new = upd ? mxc : m_run;
-            // exp2(-inf) = 0 for a row's first visible keys; rows that keep
-            // their max (fully masked ones included) keep alpha = 1
-            alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-            m_run = m_new;
+            // Lazy reference: once every row of the wave has one, exponentiate
+            // against it without taking the tile's max.  The max and the
+            // conditional rescale are taken (and P formed again) only on a
+            // row's first keys and when some lane's sum of P exceeds 2^16,
+            // so every P kept stays below 2^16 (exact in fp32 and bf16)
+            float lsum = 0.f, alpha = 1.f;
+            bool redo = !all_ref;
+            if (!redo) {
+                lsum = exps(m_run);
+                redo = __any(!(lsum <= kLazyBound));
+            }
+            if (redo) {
+                float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < D / 32; ++i)
+                for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        mx = fmaxf(mx, sacc[kb][e]);
+                mx = lane_pair_max(mx);
+                const float mxc = mx * c;
+                const bool upd = mxc > m_run + kRescaleSlack;
+                if (__any(upd)) {
+                    const float m_new = upd ? mxc : m_run;
+                    alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                    m_run = m_new;
+#pragma unroll
+                    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            oacc[i][e] *= alpha;
+                }
+                lsum = exps((m_run == -INFINITY) ? 0.f : m_run);
+                all_ref = !__any(m_run == -INFINITY);
+            }
+            l_run = l_run * alpha + lsum;
+        } else {
+            // at d = 64 (short dilated segments) the lazy reference's extra
+            // first-tile work and registers cost more than it saves
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    oacc[i][e] *= alpha;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+                    mx = fmaxf(mx, sacc[kb][e]);
+            mx = lane_pair_max(mx);
 
-        unsigned pk[BK / 32][8];
-        float lsum = 0.f;
+            // conditional rescale: raise the reference max only when some score
+            // exceeds it by more than the slack (always on a row's first keys)
+            const float mxc = mx * c;
+            const bool upd = mxc > m_run + kRescaleSlack;
+            const bool any_upd = __any(upd);
+            float alpha = 1.f;
+            if (any_upd) {
+                const float m_new = upd ? mxc : m_run;
+                // exp2(-inf) = 0 for a row's first visible keys; rows that keep
+                // their max (fully masked ones included) keep alpha = 1
+                alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                m_run = m_new;
 #pragma unroll
-        for (int kb = 0; kb < BK / 32; ++kb)
+                for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], c, -m_use));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], c, -m_use));
-                lsum += p0 + p1;
-                pk[kb][e >> 1] = pack_bf16(p0, p1);
+                    for (int e = 0; e < 16; ++e)
+                        oacc[i][e] *= alpha;
             }
-        l_run = l_run * alpha + lsum;
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+            float lsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], c, -m_use));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], c, -m_use));
+                    lsum += p0 + p1;
+                    pk[kb][e >> 1] = pack_bf16(p0, p1);
+                }
+            l_run = l_run * alpha + lsum;
+        }
 
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
