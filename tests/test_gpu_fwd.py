@@ -192,8 +192,9 @@ def test_zigzag_ring_matches_full_causal_attention_small(P, c, H, d):
     assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="zigzag ring small")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("delta", [None, 0, 150])
-def test_growing_scores_take_the_rescale_path(delta):
+def test_growing_scores_take_the_rescale_path(delta, d):
     """Keys that line up more and more with the queries: each later block of
     keys scores far above the running maximum of the earlier ones, so the
     kernel's reference maximum is raised and the accumulated O rescaled
@@ -201,7 +202,7 @@ def test_growing_scores_take_the_rescale_path(delta):
     jumps at keys 300, 500 and 700 fall in later key tiles, where the
     exponentials against the old reference overflow the lazy bound and the
     tile is redone with its max."""
-    H, N, d = 2, 900, 128
+    H, N = 2, 900
     g = torch.Generator().manual_seed(31)
     u = torch.randn(H, 1, d, generator=g)
     q = (u.expand(H, N, d) + 0.1 * torch.randn(H, N, d, generator=g)).to(torch.bfloat16)
@@ -216,7 +217,7 @@ def test_growing_scores_take_the_rescale_path(delta):
                                  out_dtype=torch.float32)
     torch.cuda.synchronize()
     sc = _np32(q)[0] @ _np32(k)[0].T / np.sqrt(d)  # head 0 scores
-    assert sc[:, 700:].max() - sc[:, :100].max() > 40  # far beyond the 2^8 slack
+    assert sc[:, 700:].max() - sc[:, :100].max() > 25  # far beyond the 2^8 slack
     assert_parity(to_np(o), to_np(lse), o_ref, l_ref, torch.bfloat16, what="growing scores")
 
 
