@@ -371,10 +371,10 @@ def longnet_split_fwd(q, k, v, segment_lengths, dilations, P: int, causal: bool 
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     lw, lr = [w for w, _ in local], [r for _, r in local]
-    for dev in range(P):
-        rows = slice(dev * share, (dev + 1) * share)
-        dilated_attn_fwd(q[..., rows, :], k[..., rows, :], v[..., rows, :], lw, lr,
-                         causal=causal, scale=scale, out=out[..., rows, :], lse=lse[..., rows])
+    # the local branches of all devices in one call: their segments never
+    # cross a device boundary (w divides the share), so this is each
+    # device's own dilated attention on its rows, batched over the devices
+    dilated_attn_fwd(q, k, v, lw, lr, causal=causal, scale=scale, out=out, lse=lse)
     for w, r in gathered:
         segs, devs = _gathered_parts(n, P, share, w, r)
         for s0, _ in segs:
@@ -406,11 +406,9 @@ def longnet_split_bwd(q, k, v, out, lse, d_o, segment_lengths, dilations, P: int
     dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
     lw, lr = [w for w, _ in local], [r for _, r in local]
-    for dev in range(P):
-        rows = slice(dev * share, (dev + 1) * share)
-        dilated_attn_bwd(q[..., rows, :], k[..., rows, :], v[..., rows, :], out[..., rows, :],
-                         lse[..., rows], d_o[..., rows, :], lw, lr, causal=causal, scale=scale,
-                         dq=dq[..., rows, :], dk=dk[..., rows, :], dv=dv[..., rows, :])
+    # local branches of all devices in one call (see longnet_split_fwd)
+    dilated_attn_bwd(q, k, v, out, lse, d_o, lw, lr, causal=causal, scale=scale,
+                     dq=dq, dk=dk, dv=dv)
     for w, r in gathered:
         segs, devs = _gathered_parts(n, P, share, w, r)
         for s0, count in segs:
