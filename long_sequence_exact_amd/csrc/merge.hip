@@ -140,7 +140,9 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(View src, View dst, int 
 unsigned grid_for(int64_t threads)
 {
     int64_t blocks = (threads + 255) / 256;
-    const int64_t cap = 256 * 64;  // enough resident waves to saturate HBM
+    // one work item per thread up to 2^26 threads: a grid-stride loop over
+    // several items per thread measured 5-7% slower on the merge
+    const int64_t cap = 256 * 1024;
     if (blocks > cap)
         blocks = cap;
     return (unsigned)(blocks > 0 ? blocks : 1);
