@@ -31,7 +31,7 @@ struct FwdParams {
     // its views move by that many tensor rows and hold
     // ceil((hs_len - h mod r) / r) rows; Nq = Nk is the count at offset 0.
     int hs_r = 0, hs_len = 0;
-    int grouped = 0;     // work order (work_item): 1 grouped by XCD
+    int grouped = 0;     // work order (work_item): 0 default, else the band
 };
 
 struct MergeParams {
@@ -52,45 +52,48 @@ struct BwdParams {
     int acc_kv;            // 1: dk, dv (fp32) are accumulated instead of written
     int hs_r = 0, hs_len = 0;  // head-dependent offsets as in FwdParams; query
                            // head h = KV head (one query head per KV head)
-    int grouped_kv = 0, grouped_q = 0;  // work order of the dK/dV and dQ launches
+    int grouped_kv = 0, grouped_q = 0;  // work order (band) of the dK/dV and dQ launches
 };
 
 // Order of a launch's work items, (group, tile) with tile 0 the longest, over
 // its workgroups.  The dispatcher hands workgroup i to XCD i mod 8, and each
-// XCD has its own L2.  Default order: the group (batch, segment, head) is
-// fastest, so every tile index is spread evenly over the XCDs, which suits
-// few groups with many tiles (long causal rows).  Grouped order, for many
-// groups with few tiles: XCD x takes groups x, x + 8, ... in bands of about
-// 32 tiles (one tile per compute unit), longest tile first within a band, so
-// a group's tiles run at about the same time and read their shared K/V (or
-// Q/dO) rows through one L2, and every XCD takes the same tile index at the
-// same slot.  The grouped launch rounds the group count up to a multiple of
-// 8; items past the last group are empty.
+// XCD has its own L2.  Default order (band 0): the group (batch, segment,
+// head) is fastest, so every tile index is spread evenly over the XCDs, which
+// suits few groups with many tiles (long causal rows).  Grouped order, for
+// many groups with few tiles: XCD x takes groups x, x + 8, ... in bands of
+// about `band` tiles (the workgroups an XCD runs at once), longest tile
+// first within a band, so a group's tiles run at about the same time and
+// read their shared K/V (or Q/dO) rows through one L2, and every XCD takes
+// the same tile index at the same slot.  The grouped launch rounds the group
+// count up to a multiple of 8; items past the last group are empty.
 constexpr int kXcds = 8;
-constexpr int kGroupMaxTiles = 32;  // one XCD's compute units
+constexpr int kXcdCUs = 32;  // compute units per XCD
 struct WorkItem {
     int grp, t;
 };
-__device__ inline WorkItem work_item(unsigned blk, int ntile, int ngrp, int grouped)
+__device__ inline WorkItem work_item(unsigned blk, int ntile, int ngrp, int band)
 {
-    if (!grouped)
+    if (!band)
         return {(int)(blk % (unsigned)ngrp), (int)(blk / (unsigned)ngrp)};
     const int xcd = (int)(blk % kXcds), j = (int)(blk / kXcds);
     const int gx = (ngrp + kXcds - 1) / kXcds;               // groups per XCD
-    const int bg = ntile < kGroupMaxTiles ? kGroupMaxTiles / ntile : 1;  // per band
-    const int band = j / (bg * ntile);
-    const int nb = min(bg, gx - band * bg);                   // groups in this band
-    const int idx = j - band * bg * ntile;
-    return {(band * bg + idx % nb) * kXcds + xcd, idx / nb};
+    const int bg = ntile < band ? band / ntile : 1;          // groups per band
+    const int bandi = j / (bg * ntile);
+    const int nb = min(bg, gx - bandi * bg);                  // groups in this band
+    const int idx = j - bandi * bg * ntile;
+    return {(bandi * bg + idx % nb) * kXcds + xcd, idx / nb};
 }
 // A dispatch counts its work-items in 32 bits.
 inline bool grid_fits(int64_t blocks, int threads)
 {
     return blocks * threads <= (int64_t)0xffffffff;
 }
-inline int use_grouped(int ntile, int ngrp)
+// Band for a launch of ngrp groups of ntile tiles whose XCDs each run `band`
+// workgroups at once: grouped when there are groups for every XCD and a
+// group's tiles fit in one band, else 0 (default order).
+inline int use_grouped(int ntile, int ngrp, int band = kXcdCUs)
 {
-    return ngrp >= kXcds && ntile <= kGroupMaxTiles;
+    return (ngrp >= kXcds && ntile <= band) ? band : 0;
 }
 inline int64_t work_items(int ntile, int ngrp, int grouped)
 {

@@ -13,8 +13,8 @@
 //   * one workgroup = 8 waves = 256 query rows of one (batch, segment, head);
 //     each wave owns 32 query rows for the whole kernel; two waves share a
 //     SIMD, so one wave's softmax VALU work overlaps the other's MFMAs;
-//   * the workgroup walks the KV segment in tiles of 128 keys, double-
-//     buffered in LDS and filled by direct HBM -> LDS buffer loads (rows past
+//   * the workgroup walks the KV segment in tiles of 128 keys (64 in
+//     non-causal launches at d = 64), double-buffered in LDS and filled by direct HBM -> LDS buffer loads (rows past
 //     the segment end read as zeros), so staging costs no VGPRs and one
 //     barrier per tile orders the fill of tile t+1 after every wave's reads
 //     of tile t-1; rows are unpadded and XOR-swizzled per 16-byte chunk so
@@ -59,7 +59,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 headroom before the max is raised
 constexpr float kLazyBound = 65536.f;  // largest lane sum of P kept without a rescale (d = 128)
-constexpr int kBK = 128;              // keys per K/V tile
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -130,10 +129,12 @@ __device__ inline float lane_pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p)
+// BK keys per K/V tile.  At d = 64 with 64-key tiles the kernel needs at most
+// 128 VGPRs and 32 KiB of LDS, so four waves share each SIMD (two
+// workgroups per CU); the other shapes run two.
+template <int D, int BK>
+__global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(const FwdParams p)
 {
-    constexpr int BK = kBK;
     constexpr int ROWB = D * 2;                  // unpadded row of D/8 16-byte chunks
     constexpr int NCH = D / 8;
     constexpr int RPP = 1024 / ROWB;             // rows per 1 KiB DMA piece
@@ -477,14 +478,21 @@ hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
     const int BH = p.B * p.S * p.Hq;
     if ((int64_t)nqt * BH == 0)
         return hipSuccess;
-    p.grouped = use_grouped(nqt, BH);
+    // non-causal d = 64 launches (LongNet's branches) take 64-key tiles at
+    // four waves per SIMD, so an XCD runs twice as many workgroups at once;
+    // causal ones keep 128-key tiles, where the larger tiles cost less than
+    // the extra waves gain
+    const bool small = d == 64 && p.noncausal;
+    p.grouped = use_grouped(nqt, BH, small ? 2 * kXcdCUs : kXcdCUs);
     const int64_t grid = work_items(nqt, BH, p.grouped);
     if (!grid_fits(grid, kThreads))
         return hipErrorInvalidConfiguration;
     if (d == 128)
-        hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 128>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    else if (small)
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     else
-        hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 128>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
