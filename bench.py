@@ -193,7 +193,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_counters(),
-                     "kernel": "fwd_bf16_kernel<128>",
+                     "kernel": "fwd_bf16_kernel<128, 128>",
                      "avg_launch_ms": round(avg_launch_ms, 4)},
         "cpu_baseline": cpu,
     }
