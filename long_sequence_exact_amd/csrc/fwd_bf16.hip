@@ -12,10 +12,12 @@
 // Work decomposition
 //   * one workgroup = 8 waves = 256 query rows of one (batch, segment, head);
 //     each wave owns 32 query rows for the whole kernel; two waves share a
-//     SIMD, so one wave's softmax VALU work overlaps the other's MFMAs;
-//   * the workgroup walks the KV segment in tiles of 128 keys (64 in
-//     non-causal launches at d = 64), double-buffered in LDS and filled by direct HBM -> LDS buffer loads (rows past
-//     the segment end read as zeros), so staging costs no VGPRs and one
+//     SIMD (four at d = 64, two workgroups per CU), so one wave's softmax
+//     VALU work can overlap another's MFMAs;
+//   * the workgroup walks the KV segment in tiles of 128 keys (64 at
+//     d = 64), double-buffered in LDS and filled by direct HBM -> LDS buffer
+//     loads (rows past the segment end read as zeros), so staging costs no
+//     VGPRs and one
 //     barrier per tile orders the fill of tile t+1 after every wave's reads
 //     of tile t-1; rows are unpadded and XOR-swizzled per 16-byte chunk so
 //     the operand reads are bank-conflict free; V stays row-major and is
@@ -478,21 +480,16 @@ hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
     const int BH = p.B * p.S * p.Hq;
     if ((int64_t)nqt * BH == 0)
         return hipSuccess;
-    // non-causal d = 64 launches (LongNet's branches) take 64-key tiles at
-    // four waves per SIMD, so an XCD runs twice as many workgroups at once;
-    // causal ones keep 128-key tiles, where the larger tiles cost less than
-    // the extra waves gain
-    const bool small = d == 64 && p.noncausal;
-    p.grouped = use_grouped(nqt, BH, small ? 2 * kXcdCUs : kXcdCUs);
+    // d = 64 launches (LongNet's branches) take 64-key tiles at four waves
+    // per SIMD, so an XCD runs twice as many workgroups at once
+    p.grouped = use_grouped(nqt, BH, d == 64 ? 2 * kXcdCUs : kXcdCUs);
     const int64_t grid = work_items(nqt, BH, p.grouped);
     if (!grid_fits(grid, kThreads))
         return hipErrorInvalidConfiguration;
     if (d == 128)
         hipLaunchKernelGGL((fwd_bf16_kernel<128, 128>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
-    else if (small)
-        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<64, 128>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
