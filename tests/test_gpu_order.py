@@ -20,6 +20,8 @@ ORDER_CASES = [
     (1, 13, 13, 520, 520, 64, 20),      # 13 groups, 3 query tiles
     (2, 10, 5, 200, 700, 128, 500),     # 20 query / 10 KV groups, GQA
     (1, 33, 11, 100, 300, 64, -40),     # 33 query / 11 KV groups
+    (1, 8, 8, 9216, 100, 64, None),     # 36 query tiles: grouped only at d = 64 (bands of 64)
+    (1, 8, 4, 9216, 100, 64, 9000),     # the same, causal, GQA
 ]
 
 
