@@ -163,3 +163,16 @@ def test_binding_rejects_host_tensors():
                      torch.zeros((1, 1, 8, 64)), torch.zeros((1, 1, 8)))
     # size queries take host descriptors
     assert sa.workspace_size(3, x, x) == 8 * 4
+
+
+def test_forward_counters_match_the_kernel_source():
+    """The HBM counters that bench.py reports as roofline traffic were taken on
+    the current forward kernel source (else bench.py reports null)."""
+    import hashlib, json, os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = os.path.join(root, "long_sequence_exact_amd", "csrc", "fwd_bf16.hip")
+    prof = os.path.join(root, "profiles", "fwd_bf16_ulysses_128k_hbm_counters.json")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    rec = json.load(open(prof))
+    assert rec["kernel_source_sha256_16"] == sha
+    assert rec["hbm_bytes_per_launch"] > 0
