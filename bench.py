@@ -24,7 +24,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 METRIC = "attention TFLOP/s (causal-adjusted) + % bf16 MFMA peak, 128K tokens, 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_ulysses_128k_hbm_counters.json")

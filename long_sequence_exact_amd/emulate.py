@@ -99,7 +99,7 @@ def _blocks(t, P, blk, first_block, count):
 
 
 def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = True,
-             lanes: int = 1):
+             lanes: int = 1, out=None, lse=None):
     """All P ranks of a ring, run one after another on one GPU.
 
     q, k, v: [B,H,N,d]; rank r owns rows [r*N/P, (r+1)*N/P).  Returns the
@@ -114,12 +114,15 @@ def ring_fwd(q, k, v, P: int, causal: bool = True, scale=None, batched: bool = T
     overlap, so one launch's epilogues (the fused merges) run while another
     computes (one stream measures fastest for the causal 16K ring, whose
     launches use the XCD-grouped work order).  batched=False issues one
-    launch per (rank, step).
+    launch per (rank, step).  out, lse: optional fp32 destinations (their
+    contents on entry are ignored: the first step writes every row).
     """
     B, H, n, d = q.shape
     blk = n // P
-    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     if not batched or B != 1 or n % P:
         for r in range(P):
             rows = slice(r * blk, (r + 1) * blk)

@@ -35,7 +35,7 @@ from . import (attn_segment_bwd, attn_segment_fwd, dilated_attn_bwd, dilated_att
                emulate, head_relayout, lse_merge)
 from .synth import WORKLOADS, draw, workload_inputs
 
-PEAK_TFLOPS = 2500.0
+PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
 PEAK_GBS = 8000.0
 
 

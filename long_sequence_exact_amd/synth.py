@@ -101,3 +101,17 @@ def workload_inputs(w: Workload, with_dout: bool = False):
     if with_dout:
         shapes.append((1, w.hq, w.nq, w.d))
     return draw(shapes, w.seed, w.dtype)
+
+
+def sample_rows_per_tile(n_total: int, tile: int, per_tile: int, seed: int, must=()):
+    """A sorted seeded subset of [0, n_total) with ``per_tile`` rows drawn in
+    every consecutive block of ``tile`` rows (fewer in a short last block),
+    always holding ``must``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    picked = set(int(m) % n_total for m in must if n_total > 0)
+    for t0 in range(0, n_total, tile):
+        n = min(tile, n_total - t0)
+        perm = torch.randperm(n, generator=g)[:min(per_tile, n)]
+        picked.update(t0 + int(x) for x in perm.tolist())
+    return sorted(picked)

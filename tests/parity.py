@@ -1,43 +1,111 @@
 """Shared helpers of the parity tests: error measures and tolerances.
 
 Tolerances (the problem statement fixes them): outputs match the fp64 oracle
-within a normwise relative error of 1e-4 for fp32 and 2e-2 for bf16 (max|x -
-ref| / max|ref| per tensor and head; element-wise relative error is unbounded
-where an output crosses zero), and LSE within 1e-3 absolute, with -inf
-entries matching exactly.
+within a maximum relative error of 1e-4 for fp32 and 2e-2 for bf16, and LSE
+within 1e-3 absolute, with -inf entries matching exactly.
+
+"Relative error" is measured per row: for row i (one query's output vector,
+or one key's gradient vector), max_c |x_ic - ref_ic| / max_c |ref_ic|.  A row
+whose reference is (nearly) zero is measured against a floor of
+ROW_FLOOR times the largest |ref| of its head, so an exactly-zero reference
+row (a query that sees no key, a key no query sees) needs an absolute match
+at that scale.  The per-row measure is at least as strict as the normwise
+one per head (max|x - ref| / max|ref|): a causal row deep in the sequence
+averages many keys and is small, so a whole run of wrong late rows can stay
+under the normwise bound, never under the per-row one.  Element-wise
+relative error is unbounded where an output crosses zero; its regularised
+form |x - ref| / (|ref| + 1e-3 max|ref|) is reported beside the gate as a
+diagnostic, as is the normwise error.
+
+With SEQATTN_PARITY_LOG set to a file path, every check appends one JSON
+line with all three measures.
 """
+import json
+import os
+
 import numpy as np
 import torch
 
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 LSE_TOL = 1e-3
+ROW_FLOOR = 1e-3
 
 
 def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def normwise_per_head(x, ref, head_axis_rows=None):
-    """Max over heads of max|x-ref|/max|ref|.  x, ref: [..., H, N, d] arrays
-    (or [rows, d] with head_axis_rows = head id per row)."""
+def _groups(x, ref, heads):
+    """(x, ref) pairs of 2-D [rows, d] arrays, one per head."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
-    if head_axis_rows is not None:
-        worst = 0.0
-        for h in np.unique(head_axis_rows):
-            sel = head_axis_rows == h
-            den = np.abs(ref[sel]).max()
-            num = np.abs(x[sel] - ref[sel]).max()
-            worst = max(worst, num / den if den > 0 else num)
-        return worst
-    x = x.reshape(-1, x.shape[-2], x.shape[-1]) if x.ndim >= 3 else x[None]
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if heads is not None:
+        heads = np.asarray(heads)
+        return [(x[heads == h], ref[heads == h]) for h in np.unique(heads)]
+    if x.ndim == 1:
+        return [(x[:, None], ref[:, None])]
+    if x.ndim == 2:
+        return [(x, ref)]
+    x = x.reshape(-1, x.shape[-2], x.shape[-1])
     ref = ref.reshape(x.shape)
-    worst = 0.0
-    for h in range(x.shape[0]):
-        den = np.abs(ref[h]).max() if ref[h].size else 0.0
-        num = np.abs(x[h] - ref[h]).max() if ref[h].size else 0.0
-        worst = max(worst, num / den if den > 0 else num)
-    return worst
+    return [(x[h], ref[h]) for h in range(x.shape[0])]
+
+
+def errors(x, ref, heads=None):
+    """Dict of the three measures, each a max over heads (and rows):
+    row   -- per-row relative error (the gate),
+    norm  -- normwise relative error per head,
+    elem  -- regularised element-wise relative error (diagnostic).
+    x, ref: [..., H, N, d] arrays, or [rows, d] with heads = head id per row."""
+    row = norm = elem = 0.0
+    for xs, rs in _groups(x, ref, heads):
+        if rs.size == 0:
+            continue
+        diff = np.abs(xs - rs)
+        if not np.all(np.isfinite(xs)):
+            return {"row": float("inf"), "norm": float("inf"), "elem": float("inf")}
+        top = np.abs(rs).max()
+        den_row = np.maximum(np.abs(rs).max(axis=-1), ROW_FLOOR * top)
+        num_row = diff.max(axis=-1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.where(den_row > 0, num_row / np.where(den_row > 0, den_row, 1), num_row)
+        row = max(row, float(r.max()))
+        norm = max(norm, float(diff.max() / top) if top > 0 else float(diff.max()))
+        e = diff / (np.abs(rs) + 1e-3 * top) if top > 0 else diff
+        elem = max(elem, float(e.max()))
+    return {"row": row, "norm": norm, "elem": elem}
+
+
+def max_rel_error(x, ref, heads=None):
+    """The gate measure: largest per-row relative error (see the module text)."""
+    return errors(x, ref, heads)["row"]
+
+
+def _log(rec):
+    path = os.environ.get("SEQATTN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+
+
+def _test_name():
+    return os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+
+
+def check_close(x, ref, tol, heads=None, what="", name="o"):
+    """Assert x (array or tensor) matches ref within tol by the per-row
+    measure, with no NaN; the message carries all three measures."""
+    if isinstance(x, torch.Tensor):
+        assert not torch.isnan(x).any(), f"{what}: NaN in {name}"
+        x = to_np(x)
+    x = np.asarray(x, np.float64)
+    assert not np.isnan(x).any(), f"{what}: NaN in {name}"
+    e = errors(x, ref, heads)
+    _log({"test": _test_name(), "what": what, "tensor": name, "tol": tol, **e})
+    assert e["row"] <= tol, (f"{what}: {name} per-row relative error {e['row']:.3e} > {tol} "
+                             f"(normwise {e['norm']:.3e}, element-wise {e['elem']:.3e})")
+    return e
 
 
 def lse_check(lse, ref):
@@ -54,13 +122,13 @@ def lse_check(lse, ref):
 
 def assert_parity(o, lse, o_ref, lse_ref, dtype, rows_heads=None, what=""):
     tol = TOL[dtype]
-    e = normwise_per_head(o, o_ref, rows_heads)
     le, same = lse_check(lse, lse_ref)
-    assert not np.isnan(np.asarray(o)).any(), f"{what}: NaN in output"
-    assert e <= tol, f"{what}: normwise relative error {e:.3e} > {tol}"
+    assert not np.isnan(np.asarray(lse)).any(), f"{what}: NaN in LSE"
+    e = check_close(o, o_ref, tol, rows_heads, what, "o")
+    _log({"test": _test_name(), "what": what, "tensor": "lse", "tol": LSE_TOL, "abs": le})
     assert le <= LSE_TOL, f"{what}: LSE error {le:.3e} > {LSE_TOL}"
     assert same, f"{what}: -inf LSE pattern differs"
-    return e, le
+    return e["row"], le
 
 
 def dilated_key_list(p, n, ws, rs, causal, shift=0):
