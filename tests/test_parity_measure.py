@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from long_sequence_exact_amd.synth import draw, sample_rows
-from tests.parity import TOL, ROW_FLOOR, errors, max_rel_error
+from tests.parity import DQ_FLOOR, TOL, ROW_FLOOR, errors, max_rel_error
 
 TOL_BF16 = TOL[torch.bfloat16]
 
@@ -80,3 +80,16 @@ def test_non_finite_output_is_an_infinite_error():
     x = ref.copy()
     x[2, 1] = np.inf
     assert max_rel_error(x, ref) == float("inf")
+
+
+def test_dq_floor_is_a_quarter_of_the_head_scale():
+    ref = np.ones((5, 4))
+    ref[0] = 1e-3                    # a near-one-hot row: tiny dQ
+    x = ref.copy()
+    x[0] += 4e-3                     # its absolute error, far above its own size
+    assert max_rel_error(x, ref) > 1.0                                  # output rule
+    assert abs(max_rel_error(x, ref, floor=DQ_FLOOR) - 4e-3 / DQ_FLOOR) < 1e-12
+    # a wrong typical row still fails under the dQ rule
+    x = ref.copy()
+    x[3] *= 0.9
+    assert max_rel_error(x, ref, floor=DQ_FLOOR) > 4 * TOL_BF16
