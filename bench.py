@@ -28,6 +28,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 METRIC = "attention TFLOP/s (causal-adjusted) + % bf16 MFMA peak, 128K tokens, 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_ulysses_128k_hbm_counters.json")
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_ulysses_128k_mfma_counters.json")
 FWD_SRC = os.path.join(ROOT, "long_sequence_exact_amd", "csrc", "fwd_bf16.hip")
 
 
@@ -53,17 +54,29 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_counters():
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel source (else None)."""
+def _fresh_counters(path):
+    """A committed rocprofv3 counter summary, if it was taken on the current
+    forward kernel source (else None)."""
     try:
-        with open(COUNTERS) as f:
+        with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
     if c.get("kernel_source_sha256_16") != source_hash(FWD_SRC):
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c
+
+
+def traffic_from_counters():
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated), or None."""
+    c = _fresh_counters(COUNTERS)
+    return c.get("hbm_bytes_per_launch") if c else None
+
+
+def mfma_busy_from_counters():
+    """Fraction of SIMD cycles with the matrix core busy, or None."""
+    c = _fresh_counters(MFMA_COUNTERS)
+    return c.get("mfma_busy") if c else None
 
 
 def cpu_baseline(q, k, v, delta, d, budget_s: float):
@@ -193,6 +206,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_counters(),
+                     "mfma_busy": mfma_busy_from_counters(),
                      "kernel": "fwd_bf16_kernel<128, 128>",
                      "avg_launch_ms": round(avg_launch_ms, 4)},
         "cpu_baseline": cpu,

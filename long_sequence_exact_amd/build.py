@@ -51,6 +51,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every symbol must resolve (a kernel whose host stub was not emitted
+    # links fine and fails only here)
+    r = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"built library does not load:\n{r.stderr.strip().splitlines()[-1]}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

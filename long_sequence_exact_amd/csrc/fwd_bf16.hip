@@ -84,6 +84,13 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, kRsrcWord3);
 }
 
+// The same for a byte count already known to fit in 31 bits (a head's rows
+// span less than 2 GiB): the clamp stays in 32-bit scalar arithmetic.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc32(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, max(bytes, 0), kRsrcWord3);
+}
+
 __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -175,8 +182,6 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
     const bf16 *V = (const bf16 *)p.v.ptr + b * p.v.sb + s * p.v.ss + g * p.v.sh + rv;
     // valid bytes of each view: rows past Nq / Nk read as zeros
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q, ((int64_t)(Nq - 1) * p.q.sn + D) * 2);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(K, Nk > 0 ? ((int64_t)(Nk - 1) * p.k.sn + D) * 2 : 0);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(V, Nk > 0 ? ((int64_t)(Nk - 1) * p.v.sn + D) * 2 : 0);
 
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + l32;
@@ -214,21 +219,32 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
     // piece u of this wave covers tile rows RPP (wave PPW + u) .. +RPP; lane L
     // fills LDS chunk L of the piece = row RPP piece + L/NCH, physical chunk
     // L%NCH, which holds logical chunk (L%NCH) ^ swizzle(row) (kswz, vswz).
+    // The lane offsets inside a tile are the same for every tile; each tile
+    // moves the buffer resources' base and size instead (scalar work), so
+    // rows past the segment end still read as zeros.
+    int koff[PPW], voff[PPW];
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int row = RPP * (wave * PPW + u) + lane / NCH;
+        const int ph = lane % NCH;
+        koff[u] = (row * (int)p.k.sn + ((ph ^ kswz<D>(row)) * 8)) * 2;
+        voff[u] = (row * (int)p.v.sn + ((ph ^ vswz<D>(row)) * 8)) * 2;
+    }
+    const int kbytes = Nk > 0 ? (int)(((int64_t)(Nk - 1) * p.k.sn + D) * 2) : 0;
+    const int vbytes = Nk > 0 ? (int)(((int64_t)(Nk - 1) * p.v.sn + D) * 2) : 0;
     auto issue_tile = [&](int t) {
         const int j0 = t * BK;
         char *kb = lds + (t & 1) * 2 * TILEB;
         char *vb = kb + TILEB;
-        int ln = lane;
-        asm volatile("" : "+v"(ln));  // recompute per tile, keep no offsets live
+        const int ks = j0 * (int)p.k.sn * 2, vs = j0 * (int)p.v.sn * 2;
+        const __amdgpu_buffer_rsrc_t kt = make_rsrc32((const char *)K + ks, kbytes - ks);
+        const __amdgpu_buffer_rsrc_t vt = make_rsrc32((const char *)V + vs, vbytes - vs);
 #pragma unroll
         for (int u = 0; u < PPW; ++u) {
             const int piece = wave * PPW + u;
-            const int row = RPP * piece + ln / NCH;
-            const int ph = ln % NCH;
-            const int ko = ((j0 + row) * (int)p.k.sn + ((ph ^ kswz<D>(row)) * 8)) * 2;
-            const int vo = ((j0 + row) * (int)p.v.sn + ((ph ^ vswz<D>(row)) * 8)) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void *)(kb + piece * 1024), 16, ko, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void *)(vb + piece * 1024), 16, vo, 0, 0, 0);
+            const int ko = koff[u], vo = voff[u];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kt, (__attribute__((address_space(3))) void *)(kb + piece * 1024), 16, ko, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vt, (__attribute__((address_space(3))) void *)(vb + piece * 1024), 16, vo, 0, 0, 0);
         }
     };
 

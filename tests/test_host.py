@@ -166,8 +166,9 @@ def test_binding_rejects_host_tensors():
 
 
 def test_forward_counters_match_the_kernel_source():
-    """The HBM counters that bench.py reports as roofline traffic were taken on
-    the current forward kernel source (else bench.py reports null)."""
+    """The HBM and MFMA counters that bench.py reports as roofline traffic and
+    mfma_busy were taken on the current forward kernel source (else bench.py
+    reports null)."""
     import hashlib, json, os
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     src = os.path.join(root, "long_sequence_exact_amd", "csrc", "fwd_bf16.hip")
@@ -176,3 +177,6 @@ def test_forward_counters_match_the_kernel_source():
     rec = json.load(open(prof))
     assert rec["kernel_source_sha256_16"] == sha
     assert rec["hbm_bytes_per_launch"] > 0
+    mfma = json.load(open(prof.replace("hbm_counters", "mfma_counters")))
+    assert mfma["kernel_source_sha256_16"] == sha
+    assert 0 < mfma["mfma_busy"] < 1
