@@ -213,6 +213,34 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              size_t workspace_bytes, void *hip_stream);
 
 /*
+ * seqattn_attn_segment_bwd_noalloc -- seqattn_attn_segment_bwd without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.
+ *
+ * Same arguments, semantics, kernels and results as seqattn_attn_segment_bwd
+ * (bit-identical).  The per-row D vector goes to a fixed 16 MiB device array
+ * inside the library instead of a workspace, so B * Hq * Nq must not exceed
+ * 4,194,304 query rows (else SEQATTN_ERR_WORKSPACE, before any HIP call).
+ * Each GPU holds its own copy of that array from the first call on that GPU
+ * until the process ends; the call itself allocates nothing.  Every call on
+ * one GPU shares the array: calls that may overlap on one GPU (on streams
+ * not ordered with each other) race, so order them.  The array keeps the
+ * last call's contents; nothing in it needs clearing between calls.
+ * Errors: as seqattn_attn_segment_bwd.
+ */
+int seqattn_attn_segment_bwd_noalloc(const seqattn_tensor *q,
+                                     const seqattn_tensor *k,
+                                     const seqattn_tensor *v,
+                                     const seqattn_tensor *o,
+                                     const seqattn_tensor *lse,
+                                     const seqattn_tensor *d_o,
+                                     int64_t causal_offset,
+                                     float softmax_scale, uint32_t flags,
+                                     seqattn_tensor *dq, seqattn_tensor *dk,
+                                     seqattn_tensor *dv, void *hip_stream);
+
+/*
  * seqattn_dilated_attn_bwd -- gradients of seqattn_dilated_attn_fwd.
  *
  * Passage: "LongNet: Scaling Transformers to 1,000,000,000 Tokens",

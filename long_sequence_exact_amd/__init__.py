@@ -21,7 +21,8 @@ from . import _lib
 from ._lib import ACCUMULATE, CAUSAL, HEAD_SHIFT, NONCAUSAL, SeqattnError
 
 __all__ = ["attn_segment_fwd", "lse_merge", "dilated_attn_fwd", "attn_segment_bwd",
-           "dilated_attn_bwd", "head_relayout", "workspace_size", "NONCAUSAL", "SeqattnError", "version"]
+           "attn_segment_bwd_noalloc", "dilated_attn_bwd", "head_relayout", "workspace_size",
+           "NONCAUSAL", "SeqattnError", "version"]
 
 
 def version() -> int:
@@ -148,6 +149,25 @@ def attn_segment_bwd(q, k, v, o, lse, d_o, causal_offset=None, scale=None, dq=No
         float(scale or 0.0), ACCUMULATE if accumulate_kv else 0, ctypes.byref(gq),
         ctypes.byref(gk), ctypes.byref(gv), ctypes.c_void_p(wptr), wbytes,
         ctypes.c_void_p(_lib.stream_handle())))
+    return dq, dk, dv
+
+
+def attn_segment_bwd_noalloc(q, k, v, o, lse, d_o, dq, dk, dv, causal_offset=None,
+                             scale=None, accumulate_kv=False):
+    """attn_segment_bwd through the entry point that allocates nothing: the
+    caller passes every output (dq accumulated, dk/dv written or, with
+    accumulate_kv, accumulated) and no workspace is used.  Calls on one GPU
+    share the library's fixed scratch, so they must not overlap."""
+    L = _lib.lib()
+    delta = NONCAUSAL if causal_offset is None else int(causal_offset)
+    ds = [_lib.desc(t) for t in (q, k, v, o)]
+    dl = _lib.desc(lse, lse=True)
+    ddo = _lib.desc(d_o)
+    gq, gk, gv = _lib.desc(dq), _lib.desc(dk), _lib.desc(dv)
+    _lib.check(L.seqattn_attn_segment_bwd_noalloc(
+        *[ctypes.byref(x) for x in ds], ctypes.byref(dl), ctypes.byref(ddo), delta,
+        float(scale or 0.0), ACCUMULATE if accumulate_kv else 0, ctypes.byref(gq),
+        ctypes.byref(gk), ctypes.byref(gv), ctypes.c_void_p(_lib.stream_handle())))
     return dq, dk, dv
 
 

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/seqattn.h"
@@ -222,6 +223,52 @@ int check_out(const seqattn_tensor *o, const seqattn_tensor *lse, const seqattn_
 }
 
 hipStream_t stream_of(void *s) { return (hipStream_t)s; }
+
+// Fixed device scratch of seqattn_attn_segment_bwd_noalloc: each GPU the
+// library runs on holds one copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, so kernels get the device address
+// that hipGetSymbolAddress returns for the device (kept per device).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `s` (the current
+// device for the null stream), looked up once per device with it current.
+int scratch_for_stream(void *s, void **out)
+{
+    int dev = 0, cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDevice");
+    dev = cur;
+    if (s) {
+        e = hipStreamGetDevice(stream_of(s), &dev);
+        if (e != hipSuccess)
+            return hip_status(e, "hipStreamGetDevice");
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SEQATTN_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds",
+                    dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return hip_status(e, "hipSetDevice");
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = e2;
+        }
+        if (e != hipSuccess)
+            return hip_status(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SEQATTN_OK;
+}
 
 // The bf16 forward addresses one head's rows with 32-bit byte offsets
 // (buffer loads, which also zero-fill rows past the end): each head's rows,
@@ -505,12 +552,17 @@ int seqattn_dilated_attn_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
     return ok();
 }
 
-int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
-                             const seqattn_tensor *v, const seqattn_tensor *o,
-                             const seqattn_tensor *lse, const seqattn_tensor *d_o,
-                             int64_t causal_offset, float softmax_scale, uint32_t flags,
-                             seqattn_tensor *dq, seqattn_tensor *dk, seqattn_tensor *dv,
-                             void *workspace, size_t workspace_bytes, void *hip_stream)
+}  // extern "C"
+
+namespace {
+
+// The segment backward; D goes to the caller's workspace, or with
+// use_scratch to the fixed per-device scratch (no workspace argument).
+int segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k, const seqattn_tensor *v,
+                const seqattn_tensor *o, const seqattn_tensor *lse, const seqattn_tensor *d_o,
+                int64_t causal_offset, float softmax_scale, uint32_t flags,
+                seqattn_tensor *dq, seqattn_tensor *dk, seqattn_tensor *dv, void *workspace,
+                size_t workspace_bytes, bool use_scratch, void *hip_stream)
 {
     int st;
     if ((st = check_qkv(q, k, v, false)))
@@ -557,10 +609,21 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
             return st;
     }
     const size_t need = seqattn_workspace_size(SEQATTN_OP_SEGMENT_BWD, q, k, 0);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(SEQATTN_ERR_WORKSPACE, "need %zu bytes of workspace", need);
-    if (workspace && (uintptr_t)workspace % 16)
-        return fail(SEQATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (use_scratch) {
+        if (need > kScratchBytes)
+            return fail(SEQATTN_ERR_WORKSPACE,
+                        "needs %zu bytes of scratch, above the fixed %zu (B*Hq*Nq <= %zu)",
+                        need, kScratchBytes, kScratchBytes / sizeof(float));
+        workspace = nullptr;
+        const bool empty = q->b == 0 || k->h == 0 || (k->n == 0 && q->n == 0);
+        if (need > 0 && !empty && (st = scratch_for_stream(hip_stream, &workspace)))
+            return st;
+    } else {
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return fail(SEQATTN_ERR_WORKSPACE, "need %zu bytes of workspace", need);
+        if (workspace && (uintptr_t)workspace % 16)
+            return fail(SEQATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    }
 
     BwdParams p;
     p.q = view_of(q);
@@ -596,6 +659,32 @@ int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
     if (e != hipSuccess)
         return hip_status(e, "attn_segment_bwd prep launch");
     return hip_status(launch_bwd_bf16(p, stream_of(hip_stream)), "attn_segment_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int seqattn_attn_segment_bwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, const seqattn_tensor *o,
+                             const seqattn_tensor *lse, const seqattn_tensor *d_o,
+                             int64_t causal_offset, float softmax_scale, uint32_t flags,
+                             seqattn_tensor *dq, seqattn_tensor *dk, seqattn_tensor *dv,
+                             void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    return segment_bwd(q, k, v, o, lse, d_o, causal_offset, softmax_scale, flags, dq, dk, dv,
+                       workspace, workspace_bytes, false, hip_stream);
+}
+
+int seqattn_attn_segment_bwd_noalloc(const seqattn_tensor *q, const seqattn_tensor *k,
+                                     const seqattn_tensor *v, const seqattn_tensor *o,
+                                     const seqattn_tensor *lse, const seqattn_tensor *d_o,
+                                     int64_t causal_offset, float softmax_scale,
+                                     uint32_t flags, seqattn_tensor *dq, seqattn_tensor *dk,
+                                     seqattn_tensor *dv, void *hip_stream)
+{
+    return segment_bwd(q, k, v, o, lse, d_o, causal_offset, softmax_scale, flags, dq, dk, dv,
+                       nullptr, 0, true, hip_stream);
 }
 
 int seqattn_dilated_attn_bwd(const seqattn_tensor *q, const seqattn_tensor *k,

@@ -277,3 +277,40 @@ def test_outputs_with_overlapping_rows_are_rejected(L):
     assert fwd(L, q, k, v, o_bad, lse) == ESTRIDE
     lse_bad = _lib.Tensor(lse.data, _lib.F32, 1, 4, 256, 1, 4 * 256, 128, 1)
     assert fwd(L, q, k, v, o, lse_bad) == ESTRIDE
+
+
+def test_bwd_noalloc_validation_errors(L):
+    """The no-allocation backward validates like the workspace one, and
+    rejects more query rows than its fixed scratch holds, before any HIP call."""
+    r = ctypes.byref
+    step = 1 << 30
+    q, k, v, o, lse = qkvo()
+    do = T(BASE + 5 * step, _lib.BF16, 1, 4, 256, 128)
+    dq = T(BASE + 6 * step, _lib.F32, 1, 4, 256, 128)
+    dk = T(BASE + 7 * step, _lib.F32, 1, 2, 512, 128)
+    dv = T(BASE + 8 * step, _lib.F32, 1, 2, 512, 128)
+
+    def call(q_=q, o_=o, lse_=lse, do_=do, dq_=dq, dk_=dk, dv_=dv, flags=0):
+        return L.seqattn_attn_segment_bwd_noalloc(r(q_), r(k), r(v), r(o_), r(lse_), r(do_), 0,
+                                                  0.0, flags, r(dq_), r(dk_), r(dv_), None)
+    dq16 = T(dq.data, _lib.BF16, 1, 4, 256, 128)
+    assert call(dq_=dq16) == EDTYPE
+    dv_al = T(dk.data + 256, _lib.F32, 1, 2, 512, 128)
+    assert call(dv_=dv_al) == EALIAS
+    assert call(flags=4) == EUNSUP
+    assert L.seqattn_attn_segment_bwd_noalloc(None, r(k), r(v), r(o), r(lse), r(do), 0, 0.0, 0,
+                                              r(dq), r(dk), r(dv), None) == ENULL
+    # 4,194,305 query rows: one more than the 16 MiB scratch holds
+    rows = (16 << 20) // 4
+    for hq, nq in ((4, rows // 4 + 1), (1, rows + 1)):
+        qb = T(BASE, _lib.BF16, 1, hq, nq, 128)
+        ob = T(BASE + 3 * step, _lib.BF16, 1, hq, nq, 128)
+        lb = LSE(BASE + 12 * step, 1, hq, nq)
+        dob = T(BASE + 5 * step, _lib.BF16, 1, hq, nq, 128)
+        dqb = T(BASE + 16 * step, _lib.F32, 1, hq, nq, 128)
+        kb = T(BASE + step, _lib.BF16, 1, 1 if hq == 1 else 2, 512, 128)
+        assert L.seqattn_attn_segment_bwd_noalloc(
+            r(qb), r(kb), r(T(BASE + 2 * step, _lib.BF16, 1, kb.h, 512, 128)), r(ob), r(lb),
+            r(dob), 0, 0.0, 0, r(dqb), r(T(dk.data, _lib.F32, 1, kb.h, 512, 128)),
+            r(T(dv.data, _lib.F32, 1, kb.h, 512, 128)), None) == EWS
+        assert "scratch" in L.seqattn_last_error().decode()
