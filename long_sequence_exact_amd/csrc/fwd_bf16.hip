@@ -106,6 +106,12 @@ __device__ inline v4i16 read_tr(const bf16 *p)
             (__attribute__((address_space(3))) bf16 *)p)));
 }
 
+// The same read at LDS byte offset `off`.
+__device__ inline v4i16 read_tr_lds(unsigned off)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(uintptr_t)off);
+}
+
 // XOR swizzles of the unpadded K and V tiles (16-byte chunk index within a
 // row).  K is read as MFMA operands, 16 lanes = 16 consecutive rows x one
 // chunk per phase: the swizzle must spread those over all 16 bank groups of
@@ -234,8 +240,8 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
     const int vbytes = Nk > 0 ? (int)(((int64_t)(Nk - 1) * p.v.sn + D) * 2) : 0;
     auto issue_tile = [&](int t) {
         const int j0 = t * BK;
-        char *kb = lds + (t & 1) * 2 * TILEB;
-        char *vb = kb + TILEB;
+        char *kb = lds + (t & 1) * TILEB;          // K buffers, then V buffers
+        char *vb = kb + 2 * TILEB;
         const int ks = j0 * (int)p.k.sn * 2, vs = j0 * (int)p.v.sn * 2;
         const __amdgpu_buffer_rsrc_t kt = make_rsrc32((const char *)K + ks, kbytes - ks);
         const __amdgpu_buffer_rsrc_t vt = make_rsrc32((const char *)V + vs, vbytes - vs);
@@ -256,24 +262,29 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
     const int vrow = 4 * (gg >> 1) + (ip >> 2);  // + 16 ks + 8 rr, same swizzle
     const int vbase = vrow * ROWB + (2 * (gg & 1) + ((ip & 3) >> 1)) * 16 + (ip & 1) * 8;
     const int vsw = vswz<D>(vrow) >> 2;
+    unsigned vlane[D / 32];  // lane offset of each 32-column block of V^T
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+        vlane[i] = vbase + ((i ^ vsw) << 6);
 
     if (ntiles > 0)
         issue_tile(0);
 
-    for (int t = 0; t < ntiles; ++t) {
+    // one tile; kbuf and vbuf are the tile's K and V buffers (the loop below
+    // runs two tiles per iteration, so both are known addresses and the LDS
+    // reads take them as immediate offsets)
+    auto step = [&](int t, const char *kbuf, const char *vbuf) {
         // tile t landed (own loads, then everyone's) and every wave is done
         // with tile t-1, whose buffer tile t+1 now fills
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 1 < ntiles)
             issue_tile(t + 1);
-        const char *kbuf = lds + (t & 1) * 2 * TILEB;
-        const char *vbuf = kbuf + TILEB;
 
         const int j0 = t * BK;
         // whole tile in this wave's causal future: nothing to compute
         if (!p.noncausal && j0 > q0w + 31 + p.delta)
-            continue;
+            return;
 
         f32x16 sacc[BK / 32];
 #pragma unroll
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
         if constexpr (D == 128) {
             // P = exp2(S c - m) rounded to bf16, and this lane's sum of P
             auto exps = [&](float m) {
-                float s0 = 0.f, s1 = 0.f;
+                float s0, s1;
 #pragma unroll
                 for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
@@ -324,8 +335,8 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
                         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], c, -m));
                         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], c, -m));
                         pk[kb][e >> 1] = pack_bf16(p0, p1);
-                        s0 += p0;
-                        s1 += p1;
+                        s0 = (kb | e) ? s0 + p0 : p0;  // the first pair starts the sums
+                        s1 = (kb | e) ? s1 + p1 : p1;
                     }
                 return s0 + s1;
             };
@@ -396,19 +407,28 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
             }
             const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-            float lsum = 0.f;
+            float lsum;
 #pragma unroll
             for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) {
                     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], c, -m_use));
                     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], c, -m_use));
-                    lsum += p0 + p1;
+                    lsum = (kb | e) ? lsum + (p0 + p1) : p0 + p1;
                     pk[kb][e >> 1] = pack_bf16(p0, p1);
                 }
             l_run = l_run * alpha + lsum;
         }
 
+        // the V buffer's LDS offset as an opaque value: the compiler then
+        // forms one base per column block and folds the key steps into the
+        // reads' offsets (a known address makes it rebuild the base per read)
+        unsigned vo = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char *)vbuf;
+        asm("" : "+s"(vo));
+        unsigned vcol[D / 32];
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+            vcol[i] = vo + vlane[i];
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int kb = ks >> 1, half = ks & 1;
@@ -417,13 +437,18 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const char *base = vbuf + 16 * ks * ROWB + vbase + ((i ^ vsw) << 6);
-                const v4i16 lo = read_tr((const bf16 *)base);
-                const v4i16 hi = read_tr((const bf16 *)(base + 8 * ROWB));
+                const unsigned base = vcol[i] + 16 * ks * ROWB;
+                const v4i16 lo = read_tr_lds(base);
+                const v4i16 hi = read_tr_lds(base + 8 * ROWB);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
             }
         }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, lds, lds + 2 * TILEB);
+        if (t + 1 < ntiles)
+            step(t + 1, lds + TILEB, lds + 3 * TILEB);
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l), optional merge ----

@@ -66,6 +66,20 @@ def dilated_pairs(n, segment_lengths, dilations, causal, shift=0):
     return tot
 
 
+def source_hashes():
+    """sha256 prefix of every HIP/C++ source the library is built from."""
+    import glob
+    import hashlib
+    import os
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    out = {}
+    for f in sorted(glob.glob(os.path.join(here, "*"))):
+        if f.endswith((".hip", ".cpp", ".h")):
+            with open(f, "rb") as fh:
+                out[os.path.basename(f)] = hashlib.sha256(fh.read()).hexdigest()[:16]
+    return out
+
+
 def warm_up(seconds=1.0):
     """Run the forward kernel untimed for about `seconds`, so the first timed
     workload does not run at ramping clocks."""
@@ -78,19 +92,26 @@ def warm_up(seconds=1.0):
         torch.cuda.synchronize()
 
 
-def timed(fn, reps, warmup=2):
+def timed(fn, reps, warmup=3, blocks=3):
+    """Per-call milliseconds: the median over `blocks` timed blocks of `reps`
+    back-to-back calls (HIP events on the launch stream), after `warmup`
+    untimed calls.  The first calls after another workload run at a lower
+    clock; the median of several blocks keeps that out."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(s)
-    for _ in range(reps):
-        fn()
-    b.record(s)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
+    per = []
+    for _ in range(blocks):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(reps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / reps)
+    return sorted(per)[len(per) // 2]
 
 
 def ring_critical_path(q, k, v, P, zigzag, reps):
@@ -287,8 +308,10 @@ def main():
                     default=["ulysses_128k_bf16", "ring_16k_bf16", "ring_16k_bf16_zigzag",
                              "longnet_32k_bf16", "longnet_page_32k_bf16",
                              "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge"])
-    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=10)
     args = ap.parse_args()
+    print(json.dumps({"kernel_sources_sha256_16": source_hashes(),
+                      "device": torch.cuda.get_device_name(0)}), flush=True)
     warm_up()
     for name in args.workload:
         print(json.dumps(run(name, args.reps)), flush=True)
