@@ -361,6 +361,17 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                // masked scores become -inf (P = 0) before the exponentials,
+                // which then run unconditionally
+                if (need_mask) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int qi = q0 + qb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                        const bool vis = (key < Nk) & (qi < Nq) &
+                                         (p.noncausal | (key - qi <= p.delta));
+                        sv[e] = vis ? sv[e] : -INFINITY;
+                    }
+                }
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int r0 = qb * 32 + gq * 8 + hl * 4;
@@ -368,16 +379,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                     const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
                     float pv[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gq * 4 + u], c, -lv[u]));
-                        if (need_mask) {
-                            const int qi = q0 + r0 + u;
-                            const bool vis = key < Nk && qi < Nq &&
-                                             (p.noncausal || key - qi <= p.delta);
-                            pe = vis ? pe : 0.f;
-                        }
-                        pv[u] = pe;
-                    }
+                    for (int u = 0; u < 4; ++u)
+                        pv[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[gq * 4 + u], c, -lv[u]));
                     pB[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
                     pB[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
                 }
@@ -645,6 +648,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_kernel(const BwdParams p)
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            // masked scores become -inf (P = 0) before the exponentials,
+            // which then run unconditionally
+            if (need_mask) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int qi = q0 + qb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                    const bool vis = (key < Nk) & (qi < Nq) &
+                                     (p.noncausal | (key - qi <= p.delta));
+                    sv[e] = vis ? sv[e] : -INFINITY;
+                }
+            }
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int r0 = qb * 32 + gq * 8 + hl * 4;
@@ -656,13 +670,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_kernel(const BwdParams p)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int e = gq * 4 + u;
-                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -lv[u]));
-                    if (need_mask) {
-                        const int qi = q0 + r0 + u;
-                        const bool vis = key < Nk && qi < Nq &&
-                                         (p.noncausal || key - qi <= p.delta);
-                        pe = vis ? pe : 0.f;
-                    }
+                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -lv[u]));
                     pv[u] = pe;
                     dsv[u] = pe * (dp[e] - dv[u]);
                 }
@@ -895,6 +903,18 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         const bool need_mask = (j0 + BK > Nk) ||
                                (!p.noncausal && j0 + BK - 1 > q0w + p.delta);
+        // masked scores become -inf (P = 0) before the exponentials, which
+        // then run unconditionally
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = j0 + kb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                    const bool vis = (key < Nk) & (p.noncausal | (key - qrow <= p.delta));
+                    s[kb][e] = vis ? s[kb][e] : -INFINITY;
+                }
+        }
         unsigned pS[BK / 32][8];
 #pragma unroll
         for (int kb = 0; kb < BK / 32; ++kb)
@@ -903,12 +923,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
                 float ds[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + u], c, -lse2));
-                    if (need_mask) {
-                        const int key = j0 + kb * 32 + ((e + u) >> 2) * 8 + hl * 4 + ((e + u) & 3);
-                        const bool vis = key < Nk && (p.noncausal || key - qrow <= p.delta);
-                        pe = vis ? pe : 0.f;
-                    }
+                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + u], c, -lse2));
                     ds[u] = pe * (dp[kb][e + u] - dq_d);
                 }
                 pS[kb][e >> 1] = pack_bf16(ds[0], ds[1]);
