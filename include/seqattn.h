@@ -146,8 +146,8 @@ int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
  * seqattn_dilated_attn_fwd -- LongNet dilated attention.
  *
  * Passage: "LongNet: Scaling Transformers to 1,000,000,000 Tokens",
- * Abstract (dilated attention as a drop-in replacement for standard
- * attention) and Results (a mixture of segment lengths w and dilation
+ * Abstract (dilated attention takes the place of dense attention with the
+ * same interface) and Results (a mixture of segment lengths w and dilation
  * ratios r).  The page's formula is not legible; the reading implemented:
  * for branch i the sequence is cut into segments of w_i tokens (the last one
  * may be shorter); a position is selected when its offset inside its segment

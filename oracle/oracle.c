@@ -17,8 +17,8 @@
  *    only combination under which the segmented result equals attention over
  *    the union of the segments);
  *  - LongNet dilated attention ("LongNet: Scaling Transformers to
- *    1,000,000,000 Tokens", Abstract and Results: a drop-in replacement for
- *    standard attention, a mixture of segment lengths w and dilation ratios
+ *    1,000,000,000 Tokens", Abstract and Results: it takes the place of
+ *    dense attention with the same interface, a mixture of segment lengths w and dilation ratios
  *    r).  The page's formula slots are empty; the reading used here is: for
  *    branch (w, r) the sequence is cut into segments of length w (the last
  *    one may be shorter), a position p is selected iff its offset inside its
