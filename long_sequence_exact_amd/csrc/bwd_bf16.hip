@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
 // ---------------------------------------------------------------------------
 
 template <int D, int BQ, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_kv_kernel(const BwdParams p)
+__device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
 {
     constexpr int kThreads = 64 * NW, kFKeys = 32 * NW;
     constexpr int CPT = BQ * D / 8 / kThreads;
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_kernel(const BwdParams p)
     const int gg = lane >> 4, ip = lane & 15;
 
     const int nkt = (p.Nk + kFKeys - 1) / kFKeys;
-    const WorkItem wi = work_item(blockIdx.x, nkt, p.B * p.S * p.Hkv, p.grouped_kv);
+    const WorkItem wi = work_item(blk, nkt, p.B * p.S * p.Hkv, p.grouped_kv);
     if (wi.grp >= p.B * p.S * p.Hkv)
         return;  // padding item of a grouped launch
     const int kt = wi.t;
@@ -765,7 +765,7 @@ struct QCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
+__device__ __forceinline__ void bwd_dq_body(const BwdParams &p, unsigned blk)
 {
     using C = QCfg<D>;
     constexpr int BK = C::BK;
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
 
     const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
     const int BH = p.B * p.S * p.Hq;
-    const WorkItem wi = work_item(blockIdx.x, nqt, BH, p.grouped_q);
+    const WorkItem wi = work_item(blk, nqt, BH, p.grouped_q);
     if (wi.grp >= BH)
         return;  // padding item of a grouped launch
     const int qt = nqt - 1 - wi.t;  // longest first
@@ -971,6 +971,29 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
         }
 }
 
+template <int D>
+__global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdParams p)
+{
+    bwd_dq_body<D>(p, blockIdx.x);
+}
+
+// dK/dV and dQ of one segment call in one launch (d = 64): blocks below nkv
+// run dK/dV items, blocks from nkv_pad on run dQ items (nkv rounded up to a
+// multiple of the XCD count, so both kinds keep their XCD-aware order).  The
+// two kinds write different outputs and read only the inputs and D, so they
+// may run side by side; one launch fills the chip where either alone would
+// not (LongNet's long-segment branches select few rows) and drains once.
+template <int D, int BQ, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_kvdq_kernel(const BwdParams p, unsigned nkv,
+                                                            unsigned nkv_pad)
+{
+    static_assert(64 * NW == kQThreads, "both kinds of item use the same workgroup");
+    if (blockIdx.x < nkv)
+        bwd_kv_body<D, BQ, NW>(p, blockIdx.x);
+    else if (blockIdx.x >= nkv_pad)
+        bwd_dq_body<D>(p, blockIdx.x - nkv_pad);
+}
+
 unsigned zero_grid(int64_t threads)
 {
     int64_t blocks = (threads + 255) / 256;
@@ -1012,27 +1035,32 @@ hipError_t launch_bwd_bf16(const BwdParams &p0, hipStream_t st)
     const int64_t grid = (int64_t)nkt * BSG == 0 ? 0 : work_items(nkt, BSG, p.grouped_kv);
     if (!grid_fits(grid, kThreads))
         return hipErrorInvalidConfiguration;
+    const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
+    const int BH = p.B * p.S * p.Hq;
+    const bool dq_work = (int64_t)nqt * BH > 0 && p.Nk > 0;
+    p.grouped_q = use_grouped(nqt, BH);
+    const int64_t qgrid = dq_work ? work_items(nqt, BH, p.grouped_q) : 0;
+    if (p.d == 64) {
+        const int64_t pad = (grid + kXcds - 1) / kXcds * kXcds;
+        if (!grid_fits(pad + qgrid, kQThreads))
+            return hipErrorInvalidConfiguration;
+        if (pad + qgrid == 0)
+            return hipSuccess;
+        hipLaunchKernelGGL((bwd_kvdq_kernel<64, kBQ, 8>), dim3((unsigned)(pad + qgrid)),
+                           dim3(kQThreads), 0, st, p, (unsigned)grid, (unsigned)pad);
+        return hipGetLastError();
+    }
     if (grid > 0) {
-        if (p.d == 128)
-            hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
-        else
-            hipLaunchKernelGGL((bwd_kv_kernel<64, kBQ, 8>), dim3((unsigned)grid), dim3(512), 0, st, p);
+        hipLaunchKernelGGL(bwd_main_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    const int nqt = (p.Nq + kQBQ - 1) / kQBQ;
-    const int BH = p.B * p.S * p.Hq;
-    if ((int64_t)nqt * BH == 0 || p.Nk == 0)
+    if (!dq_work)
         return hipSuccess;
-    p.grouped_q = use_grouped(nqt, BH);
-    const int64_t qgrid = work_items(nqt, BH, p.grouped_q);
     if (!grid_fits(qgrid, kQThreads))
         return hipErrorInvalidConfiguration;
-    if (p.d == 128)
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)qgrid), dim3(kQThreads), 0, st, p);
     return hipGetLastError();
 }
 
