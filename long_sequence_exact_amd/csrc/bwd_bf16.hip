@@ -8,7 +8,8 @@
 // reduce-scatter).  With P = exp(sigma*S - LSE) and D_i = dO_i . O_i:
 //   dV = P^T dO,  dS = P o (dO V^T - D),  dK = sigma dS^T Q,  dQ += sigma dS K.
 //
-// Work decomposition (three launches)
+// Work decomposition (three launches at d = 128; at d = 64 the dK/dV and dQ
+// items share one launch, bwd_kvdq)
 //   * bwd_prep: D_i for every query row (HBM-bound, 16 lanes per row, rows
 //     strided over a capped grid);
 //   * bwd_main (dK, dV, d = 128): one workgroup = 8 waves for 128 keys of one
