@@ -13,7 +13,10 @@
 //   * one workgroup = 8 waves = 256 query rows of one (batch, segment, head);
 //     each wave owns 32 query rows for the whole kernel; two waves share a
 //     SIMD (four at d = 64, two workgroups per CU), so one wave's softmax
-//     VALU work can overlap another's MFMAs;
+//     VALU work can overlap another's MFMAs.  Two other shapes: a long
+//     d = 128 call that writes its own output takes 12 waves (384 rows,
+//     three per SIMD) with 64-key tiles, and a d = 64 launch too small to
+//     fill the chip takes 4 waves (128 rows, four workgroups per CU);
 //   * the workgroup walks the KV segment in tiles of 128 keys (64 at
 //     d = 64), double-buffered in LDS and filled by direct HBM -> LDS buffer
 //     loads (rows past the segment end read as zeros), so staging costs no
@@ -144,17 +147,21 @@ __device__ inline float lane_pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// BK keys per K/V tile.  At d = 64 with 64-key tiles the kernel needs at most
-// 128 VGPRs and 32 KiB of LDS, so four waves share each SIMD (two
-// workgroups per CU); the other shapes run two.
-template <int D, int BK>
-__global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(const FwdParams p)
+// BK keys per K/V tile, NW waves (32 query rows each) per workgroup.  Shapes
+// launched: d = 128 with 128-key tiles, 8 waves, two per SIMD; d = 128 with
+// 64-key tiles, 12 waves, three per SIMD (168 VGPRs); d = 64 with 64-key
+// tiles (at most 128 VGPRs, 32 KiB of LDS), four waves per SIMD: two 8-wave
+// or four 4-wave workgroups per CU.
+template <int D, int BK, int NW = kWaves>
+__global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd_bf16_kernel(const FwdParams p)
 {
+    constexpr int kBQ = 32 * NW;
     constexpr int ROWB = D * 2;                  // unpadded row of D/8 16-byte chunks
     constexpr int NCH = D / 8;
     constexpr int RPP = 1024 / ROWB;             // rows per 1 KiB DMA piece
     constexpr int TILEB = BK * ROWB;             // bytes per K or V tile
-    constexpr int PPW = TILEB / 1024 / kWaves;   // DMA pieces per wave
+    constexpr int NPC = TILEB / 1024;            // DMA pieces per tile
+    constexpr int PPW = (NPC + NW - 1) / NW;     // DMA pieces per wave (at most)
     __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILEB];
 
     const int tid = threadIdx.x;
@@ -221,20 +228,23 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
     bool all_ref = false;     // every row of the wave has a finite reference
     const float c = p.scale * kLog2e;
 
-    // K/V tiles go HBM -> LDS by direct buffer loads into unpadded rows:
-    // piece u of this wave covers tile rows RPP (wave PPW + u) .. +RPP; lane L
-    // fills LDS chunk L of the piece = row RPP piece + L/NCH, physical chunk
-    // L%NCH, which holds logical chunk (L%NCH) ^ swizzle(row) (kswz, vswz).
-    // The lane offsets inside a tile are the same for every tile; each tile
-    // moves the buffer resources' base and size instead (scalar work), so
-    // rows past the segment end still read as zeros.
-    int koff[PPW], voff[PPW];
-#pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-        const int row = RPP * (wave * PPW + u) + lane / NCH;
+    // K/V tiles go HBM -> LDS by direct buffer loads into unpadded rows, in
+    // 1 KiB pieces: this wave loads pieces wave + NW u (u = 0, 1, ...), piece
+    // i covering tile rows RPP i .. +RPP; lane L fills LDS chunk L of the
+    // piece = row RPP i + L/NCH, physical chunk L%NCH, which holds logical
+    // chunk (L%NCH) ^ swizzle(row) (kswz, vswz).  Piece wave + NW u lies
+    // RPP NW u rows below piece `wave`, a multiple of both swizzles' period
+    // (16 rows), so all of a wave's pieces share one lane offset and differ
+    // by a scalar offset.  The lane offsets are also the same for every
+    // tile; each tile moves the buffer resources' base and size instead
+    // (scalar work), so rows past the segment end still read as zeros.
+    static_assert(PPW == 1 || (RPP * NW) % 16 == 0, "pieces of a wave share the swizzle");
+    int koff, voff;
+    {
+        const int row = RPP * wave + lane / NCH;
         const int ph = lane % NCH;
-        koff[u] = (row * (int)p.k.sn + ((ph ^ kswz<D>(row)) * 8)) * 2;
-        voff[u] = (row * (int)p.v.sn + ((ph ^ vswz<D>(row)) * 8)) * 2;
+        koff = (row * (int)p.k.sn + ((ph ^ kswz<D>(row)) * 8)) * 2;
+        voff = (row * (int)p.v.sn + ((ph ^ vswz<D>(row)) * 8)) * 2;
     }
     const int kbytes = Nk > 0 ? (int)(((int64_t)(Nk - 1) * p.k.sn + D) * 2) : 0;
     const int vbytes = Nk > 0 ? (int)(((int64_t)(Nk - 1) * p.v.sn + D) * 2) : 0;
@@ -247,10 +257,13 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
         const __amdgpu_buffer_rsrc_t vt = make_rsrc32((const char *)V + vs, vbytes - vs);
 #pragma unroll
         for (int u = 0; u < PPW; ++u) {
-            const int piece = wave * PPW + u;
-            const int ko = koff[u], vo = voff[u];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kt, (__attribute__((address_space(3))) void *)(kb + piece * 1024), 16, ko, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vt, (__attribute__((address_space(3))) void *)(vb + piece * 1024), 16, vo, 0, 0, 0);
+            const int piece = wave + NW * u;
+            if (NPC % NW != 0 && piece >= NPC)
+                break;
+            const int ko = koff, vo = voff;
+            const int ksu = u * RPP * NW * (int)p.k.sn * 2, vsu = u * RPP * NW * (int)p.v.sn * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kt, (__attribute__((address_space(3))) void *)(kb + piece * 1024), 16, ko, ksu, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vt, (__attribute__((address_space(3))) void *)(vb + piece * 1024), 16, vo, vsu, 0, 0);
         }
     };
 
@@ -517,20 +530,51 @@ __global__ __launch_bounds__(kThreads, BK == 64 ? 4 : 2) void fwd_bf16_kernel(co
 hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
 {
     FwdParams p = p0;
-    const int nqt = (p.Nq + kBQ - 1) / kBQ;
     const int BH = p.B * p.S * p.Hq;
+    int nqt = (p.Nq + kBQ - 1) / kBQ;
     if ((int64_t)nqt * BH == 0)
         return hipSuccess;
+    if (d == 128 && !p.accumulate && p.Nq >= 16384) {
+        // a long call writing its own output (the Ulysses share): 12-wave
+        // workgroups of 384 rows, three waves per SIMD, measured 1-2% faster
+        // there; the accumulating sweeps (ring and USP steps) and short
+        // blocks keep 8 waves (384 does not divide their 2048-row blocks)
+        nqt = (p.Nq + 383) / 384;
+        p.grouped = use_grouped(nqt, BH, kXcdCUs);
+        const int64_t grid = work_items(nqt, BH, p.grouped);
+        if (!grid_fits(grid, 768))
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 12>), dim3((unsigned)grid), dim3(768), 0, st, p);
+        return hipGetLastError();
+    }
+    if (d == 128) {
+        p.grouped = use_grouped(nqt, BH, kXcdCUs);
+        const int64_t grid = work_items(nqt, BH, p.grouped);
+        if (!grid_fits(grid, kThreads))
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 128>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+        return hipGetLastError();
+    }
     // d = 64 launches (LongNet's branches) take 64-key tiles at four waves
-    // per SIMD, so an XCD runs twice as many workgroups at once
-    p.grouped = use_grouped(nqt, BH, d == 64 ? 2 * kXcdCUs : kXcdCUs);
+    // per SIMD: two 8-wave workgroups per CU, so an XCD runs twice as many
+    // at once.  A launch with fewer workgroups than the chip holds (a
+    // long-segment branch selects few rows) takes 4-wave workgroups of 128
+    // rows instead, four per CU, so its rows spread over twice as many CUs
+    const bool small = (int64_t)nqt * BH < 2 * 256;
+    if (small) {
+        nqt = (p.Nq + 127) / 128;
+        p.grouped = use_grouped(nqt, BH, 4 * kXcdCUs);
+        const int64_t grid = work_items(nqt, BH, p.grouped);
+        if (!grid_fits(grid, 256))
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 4>), dim3((unsigned)grid), dim3(256), 0, st, p);
+        return hipGetLastError();
+    }
+    p.grouped = use_grouped(nqt, BH, 2 * kXcdCUs);
     const int64_t grid = work_items(nqt, BH, p.grouped);
     if (!grid_fits(grid, kThreads))
         return hipErrorInvalidConfiguration;
-    if (d == 128)
-        hipLaunchKernelGGL((fwd_bf16_kernel<128, 128>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -352,6 +352,47 @@ def test_ulysses_128k_full_size_sampled():
                   what="ulysses 128k")
 
 
+LONG_CASES = [
+    # (hq, hkv, nq, nk, delta, out dtype)
+    (2, 1, 16384 + 77, 16384 + 77, 0, torch.bfloat16),       # causal, ragged last tile
+    (2, 2, 16384 + 300, 20000, -700, torch.float32),          # early rows see no key
+    (3, 1, 17000, 5000, None, torch.bfloat16),                # non-causal, ragged key tail
+    (1, 1, 16384, 16384 + 999, 999, torch.float32),           # keys ahead of the queries
+]
+
+
+@pytest.mark.parametrize("hq,hkv,nq,nk,delta,odt", LONG_CASES)
+def test_long_call_shape(hq, hkv, nq, nk, delta, odt):
+    """Long d = 128 calls that write their own output (at least 16384 query
+    rows) run with 384-row workgroups.  O and LSE start as NaN; every O row
+    must come back finite, every LSE row finite or -inf exactly where the
+    oracle says the row sees no key; one seeded row in every 32-row slice of
+    every head against the oracle."""
+    d = 128
+    q, k, v = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d)], 1400 + nq + hq)
+    out = torch.full(q.shape, float("nan"), dtype=odt, device=DEV)
+    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device=DEV)
+    sa.attn_segment_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal_offset=delta, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "unwritten or non-finite O rows"
+    assert not torch.isnan(lse).any(), "unwritten LSE rows"
+    rows = []
+    for h in range(hq):
+        rows += [h * nq + i for i in sample_rows_per_tile(nq, 32, 1, 1500 + h, must=(0, nq - 1))]
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=_delta_arg(delta),
+                                   rows=rows)
+    og = to_np(out).reshape(-1, d)[rows]
+    lg = to_np(lse).reshape(-1)[rows]
+    if delta is not None and delta < 0:
+        # rows with no visible key: O = 0, LSE = -inf (all of them, not only sampled)
+        empty = torch.arange(nq) + delta < 0
+        assert torch.isneginf(lse.cpu()[0][:, empty]).all()
+        assert (out.cpu()[0][:, empty] == 0).all()
+    assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // nq,
+                  what=f"long call {nq}x{nk}")
+
+
 def test_usp_forward_full_size_sampled():
     """GQA 8/2, d=128, query block 7 of 8 (32768 rows) swept over 8 KV blocks
     of 32768, accumulator NaN-filled first (every row must come back
