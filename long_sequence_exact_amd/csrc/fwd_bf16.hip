@@ -457,6 +457,18 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
             }
         }
+        if constexpr (NW == 12) {
+            // keep four MFMAs' transposed V reads (two each) in flight; at
+            // three waves per SIMD the compiler's own order keeps about two
+            constexpr int NM = (BK / 16) * (D / 32);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int u = 0; u < NM - 4; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
     };
     for (int t = 0; t < ntiles; t += 2) {
         step(t, lds, lds + 2 * TILEB);
