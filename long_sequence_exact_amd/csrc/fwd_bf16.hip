@@ -457,9 +457,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
             }
         }
-        if constexpr (NW == 12) {
-            // keep four MFMAs' transposed V reads (two each) in flight; at
-            // three waves per SIMD the compiler's own order keeps about two
+        if constexpr (D == 128) {
+            // keep four MFMAs' transposed V reads (two each) in flight (the
+            // compiler's own order keeps about two)
             constexpr int NM = (BK / 16) * (D / 32);
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
