@@ -6,7 +6,8 @@ import torch
 import oracle
 import long_sequence_exact_amd as sa
 from long_sequence_exact_amd import emulate
-from long_sequence_exact_amd.synth import WORKLOADS, draw, sample_rows, workload_inputs
+from long_sequence_exact_amd.synth import (WORKLOADS, draw, sample_rows, sample_rows_per_tile,
+                                           workload_inputs)
 from tests.parity import TOL, assert_parity, check_close, dilated_key_list, to_np
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +47,27 @@ def test_dilated_small(n, d, hq, hkv, ws, rs, causal):
                                  out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_parity(to_np(ob), to_np(lb), o_ref, l_ref, torch.bfloat16, what="dilated bf16 out")
+
+
+def test_dilated_long_dense_first_branch_d128():
+    """A first branch with r = 1 over a segment of at least 16384 rows writes
+    the accumulator directly and runs with 384-row workgroups; the second
+    branch merges into it.  O and LSE must be fully written; one seeded row
+    in every 32-row slice of both heads against the oracle."""
+    n, d, hq, hkv = 16384 + 96, 128, 2, 1
+    ws, rs = (n, 4096), (1, 2)
+    q, k, v = draw([(1, hq, n, d), (1, hkv, n, d), (1, hkv, n, d)], 560)
+    o, lse = sa.dilated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), ws, rs, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rows = []
+    for h in range(hq):
+        rows += [h * n + i for i in sample_rows_per_tile(n, 32, 1, 570 + h, must=(0, n - 1))]
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.dilated_fwd(_np32(q), _np32(k), _np32(v), ws, rs, causal=True,
+                                      rows=rows)
+    assert_parity(to_np(o).reshape(-1, d)[rows], to_np(lse).reshape(-1)[rows], o_ref, l_ref,
+                  torch.bfloat16, rows_heads=rows // n, what="dilated long dense first branch")
 
 
 HEAD_SHIFT_CASES = [
