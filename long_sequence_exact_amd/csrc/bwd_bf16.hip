@@ -49,6 +49,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBKV = 128;          // keys per workgroup (32 per wave pair)
 constexpr int kBQ = 64;            // query rows per iteration
 constexpr float kLog2e = 1.4426950408889634f;
+// MFMAs' worth of LDS operand reads kept in flight in the d = 64 blocks (the
+// d = 128 kernels keep four: six measured no faster there, and slower in the
+// dK/dV kernel)
+constexpr int AHEAD = 6;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -642,13 +646,14 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
                 sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kB[kk], sv, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vB[kk], dp, 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            constexpr int A = AHEAD;
+            __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
-            for (int u = 0; u < 2 * (D / 16) - 4; ++u) {
+            for (int u = 0; u < 2 * (D / 16) - A; ++u) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
             // masked scores become -inf (P = 0) before the exponentials,
             // which then run unconditionally
             if (need_mask) {
@@ -703,13 +708,13 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
                 accK[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bd, accK[i], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
 #pragma unroll
-        for (int u = 0; u < 2 * (BQ / 16) * (D / 32) - 4; ++u) {
+        for (int u = 0; u < 2 * (BQ / 16) * (D / 32) - AHEAD; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
     }
 
     if (key >= Nk)
@@ -894,14 +899,15 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p, unsigned blk)
                 dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
             }
         }
-        // keep four operand reads in flight ahead of the MFMA that uses them
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // keep operand reads in flight ahead of the MFMA that uses them
+        constexpr int A = D == 64 ? AHEAD : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
-        for (int u = 0; u < 2 * (BK / 32) * (D / 16) - 4; ++u) {
+        for (int u = 0; u < 2 * (BK / 32) * (D / 16) - A; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
         const bool need_mask = (j0 + BK > Nk) ||
                                (!p.noncausal && j0 + BK - 1 > q0w + p.delta);
         // masked scores become -inf (P = 0) before the exponentials, which
@@ -945,13 +951,14 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p, unsigned blk)
             }
         }
         // two transposing reads per MFMA; keep four MFMAs' worth in flight
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        constexpr int A2 = D == 64 ? AHEAD : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * A2, 0);
 #pragma unroll
-        for (int u = 0; u < (BK / 16) * (D / 32) - 4; ++u) {
+        for (int u = 0; u < (BK / 16) * (D / 32) - A2; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, A2, 0);
     }
 
     if (qrow >= Nq)
