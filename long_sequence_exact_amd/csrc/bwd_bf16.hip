@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         }
         if (tid < BQ) {
             lse2s[buf][tid] = lreg;
-            Dsh[buf][tid] = dreg;
+            Dsh[buf][tid] = -dreg;  // -D: the dP accumulators start from it
         }
     };
 
@@ -396,10 +396,16 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         } else {
 #pragma unroll
             for (int qb = 0; qb < BQ / 32; ++qb) {
+                // dP - D: the accumulator starts at -D of its query rows
                 f32x16 dp;
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    dp[e] = 0.f;
+                for (int gq = 0; gq < 4; ++gq) {
+                    const float4 nd = *(const float4 *)(&Dsh[buf][qb * 32 + gq * 8 + hl * 4]);
+                    dp[gq * 4 + 0] = nd.x;
+                    dp[gq * 4 + 1] = nd.y;
+                    dp[gq * 4 + 2] = nd.z;
+                    dp[gq * 4 + 3] = nd.w;
+                }
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
                     const bf16x8 ad = *(const bf16x8 *)(Ob + swz_off<D>(qb * 32 + l32, 2 * kk + hl));
@@ -418,13 +424,11 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
                 const unsigned pw[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int r0 = qb * 32 + gq * 8 + hl * 4;
-                    const float4 dd = *(const float4 *)(&Dsh[buf][r0]);
                     const unsigned a0 = pw[gq * 2 + 0], a1 = pw[gq * 2 + 1];
-                    const float d0 = bf16_lo(a0) * (dp[gq * 4 + 0] - dd.x);
-                    const float d1 = bf16_hi(a0) * (dp[gq * 4 + 1] - dd.y);
-                    const float d2 = bf16_lo(a1) * (dp[gq * 4 + 2] - dd.z);
-                    const float d3 = bf16_hi(a1) * (dp[gq * 4 + 3] - dd.w);
+                    const float d0 = bf16_lo(a0) * dp[gq * 4 + 0];
+                    const float d1 = bf16_hi(a0) * dp[gq * 4 + 1];
+                    const float d2 = bf16_lo(a1) * dp[gq * 4 + 2];
+                    const float d3 = bf16_hi(a1) * dp[gq * 4 + 3];
                     pB[qb][gq * 2 + 0] = pack_bf16(d0, d1);
                     pB[qb][gq * 2 + 1] = pack_bf16(d2, d3);
                 }
@@ -620,7 +624,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
         }
         if (tid < BQ) {
             lse2s[tid] = lreg;
-            Dsh[tid] = dreg;
+            Dsh[tid] = -dreg;  // -D: the dP accumulators start from it
         }
         __syncthreads();
         if (it + 1 < niters)
@@ -634,10 +638,19 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
         unsigned pB[BQ / 32][8], dB[BQ / 32][8];  // P and dS, bf16 pairs
 #pragma unroll
         for (int qb = 0; qb < BQ / 32; ++qb) {
+            // dP - D: the dP accumulator starts at -D of its query rows
             f32x16 sv, dp;
 #pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const float4 nd = *(const float4 *)(&Dsh[qb * 32 + gq * 8 + hl * 4]);
+                dp[gq * 4 + 0] = nd.x;
+                dp[gq * 4 + 1] = nd.y;
+                dp[gq * 4 + 2] = nd.z;
+                dp[gq * 4 + 3] = nd.w;
+            }
+#pragma unroll
             for (int e = 0; e < 16; ++e)
-                sv[e] = dp[e] = 0.f;
+                sv[e] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
                 const int off = swz_off<D>(qb * 32 + l32, 2 * kk + hl);
@@ -669,16 +682,14 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
             for (int gq = 0; gq < 4; ++gq) {
                 const int r0 = qb * 32 + gq * 8 + hl * 4;
                 const float4 l2 = *(const float4 *)(&lse2s[r0]);
-                const float4 dd = *(const float4 *)(&Dsh[r0]);
                 const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-                const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
                 float pv[4], dsv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int e = gq * 4 + u;
                     const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -lv[u]));
                     pv[u] = pe;
-                    dsv[u] = pe * (dp[e] - dv[u]);
+                    dsv[u] = pe * dp[e];
                 }
                 pB[qb][gq * 2 + 0] = pack_bf16(pv[0], pv[1]);
                 pB[qb][gq * 2 + 1] = pack_bf16(pv[2], pv[3]);
