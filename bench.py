@@ -15,7 +15,6 @@ fp64 CPU oracle timed on a bounded, seeded row sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -50,8 +49,9 @@ def visible_pairs(nq: int, nk: int, delta: int | None) -> int:
 
 
 def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of a kernel source and its extra compile flags."""
+    from long_sequence_exact_amd.build import source_digest
+    return source_digest(path)
 
 
 def _fresh_counters(path):

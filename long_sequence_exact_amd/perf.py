@@ -67,16 +67,16 @@ def dilated_pairs(n, segment_lengths, dilations, causal, shift=0):
 
 
 def source_hashes():
-    """sha256 prefix of every HIP/C++ source the library is built from."""
+    """sha256 prefix of every HIP/C++ source the library is built from (with
+    its extra compile flags, if any)."""
     import glob
-    import hashlib
     import os
+    from .build import source_digest
     here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
     out = {}
     for f in sorted(glob.glob(os.path.join(here, "*"))):
         if f.endswith((".hip", ".cpp", ".h")):
-            with open(f, "rb") as fh:
-                out[os.path.basename(f)] = hashlib.sha256(fh.read()).hexdigest()[:16]
+            out[os.path.basename(f)] = source_digest(f)
     return out
 
 

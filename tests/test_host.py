@@ -167,13 +167,14 @@ def test_binding_rejects_host_tensors():
 
 def test_forward_counters_match_the_kernel_source():
     """The HBM and MFMA counters that bench.py reports as roofline traffic and
-    mfma_busy were taken on the current forward kernel source (else bench.py
-    reports null)."""
-    import hashlib, json, os
+    mfma_busy were taken on the current forward kernel source and compile
+    flags (else bench.py reports null)."""
+    import json, os
+    from long_sequence_exact_amd.build import source_digest
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     src = os.path.join(root, "long_sequence_exact_amd", "csrc", "fwd_bf16.hip")
     prof = os.path.join(root, "profiles", "fwd_bf16_ulysses_128k_hbm_counters.json")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = source_digest(src)
     rec = json.load(open(prof))
     assert rec["kernel_source_sha256_16"] == sha
     assert rec["hbm_bytes_per_launch"] > 0
