@@ -14,9 +14,10 @@
 //     each wave owns 32 query rows for the whole kernel; two waves share a
 //     SIMD (four at d = 64, two workgroups per CU), so one wave's softmax
 //     VALU work can overlap another's MFMAs.  Two other shapes: a long
-//     d = 128 call that writes its own output takes 12 waves (384 rows,
-//     three per SIMD) with 64-key tiles, and a d = 64 launch too small to
-//     fill the chip takes 4 waves (128 rows, four workgroups per CU);
+//     d = 128 call that writes its own output, with enough query tiles for
+//     four workgroups per CU, takes 12 waves (384 rows, three per SIMD) with
+//     64-key tiles, and a d = 64 launch too small to fill the chip takes 4
+//     waves (128 rows, four workgroups per CU);
 //   * the workgroup walks the KV segment in tiles of 128 keys (64 at
 //     d = 64), double-buffered in LDS and filled by direct HBM -> LDS buffer
 //     loads (rows past the segment end read as zeros), so staging costs no
@@ -546,12 +547,18 @@ hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
     int nqt = (p.Nq + kBQ - 1) / kBQ;
     if ((int64_t)nqt * BH == 0)
         return hipSuccess;
-    if (d == 128 && !p.accumulate && p.Nq >= 16384) {
-        // a long call writing its own output (the Ulysses share): 12-wave
-        // workgroups of 384 rows, three waves per SIMD, measured 1-2% faster
-        // there; the accumulating sweeps (ring and USP steps) and short
-        // blocks keep 8 waves (384 does not divide their 2048-row blocks)
-        nqt = (p.Nq + 383) / 384;
+    const int nqt12 = (p.Nq + 383) / 384;
+    if (d == 128 && !p.accumulate && p.Nq >= 16384 &&
+        (int64_t)nqt12 * BH >= 4 * kXcds * kXcdCUs) {
+        // a long call writing its own output (the Ulysses share at 128K
+        // tokens): 12-wave workgroups of 384 rows, three waves per SIMD,
+        // measured 1-2% faster there.  It needs at least four workgroups per
+        // CU: with fewer, the causal call's longest workgroups set its time
+        // and the 8-wave kernel's finer tiles finish sooner (64K tokens, 4
+        // heads: 3.63 against 3.76 ms).  The accumulating sweeps (ring and
+        // USP steps) and short blocks keep 8 waves (384 does not divide
+        // their 2048-row blocks)
+        nqt = nqt12;
         p.grouped = use_grouped(nqt, BH, kXcdCUs);
         const int64_t grid = work_items(nqt, BH, p.grouped);
         if (!grid_fits(grid, 768))

@@ -9,7 +9,8 @@ the launch stream, inputs already resident in HBM:
                       over 2 streams)
   ring_16k_bf16_zigzag  the same with the load-balanced zigzag split (ranks over
                       2 streams; also timed on one)
-  ulysses_128k_bf16   one causal forward launch (the benchmark's step)
+  ulysses_128k_bf16   one causal forward launch (the benchmark's step); also the
+                      same input as 8 KV segments of 16384 through the fused merge
   longnet_32k_bf16    dilated attention, 5 branches merged by LSE; its backward
   longnet_page_32k_bf16  causal, r = 1,2,4,6,12: single-GPU and split over 4
                       emulated devices (all-gathered long segments), fwd + bwd;
@@ -19,6 +20,8 @@ the launch stream, inputs already resident in HBM:
                       buffer [8][16384][4][128] and back, in GB/s
   lse_merge           standalone merge of two [32, 16384, 128] partials
                       (fp32 accumulator + bf16 partial), reported in GB/s
+  ulysses_len_sweep   the 128K call's shape (4 heads, d = 128, causal, one
+                      launch) at 16K, 32K, 64K, 128K and 256K tokens
 FLOPs are algorithmic (4*d per visible pair forward, 10*d backward); bytes
 for the merge are the tensors read and written.  The ring lines also time
 every (rank, step) call alone, as on a device of its own, and report the
@@ -213,6 +216,27 @@ def run(name, reps):
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
         ms = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=0, out=out, lse=lse), reps)
         fl = 4.0 * w.d * w.hq * pairs(w.nq, w.nk, 0)
+        # the same input as 8 KV segments of 16384 through the fused merge
+        del out
+        acc = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        ms_s = timed(lambda: emulate.sweep_fwd(q, k, v, 8, 0, True, acc, lse), reps)
+    elif name == "ulysses_len_sweep":
+        # the 128K call's shape (4 heads, d = 128, causal, one launch) at
+        # 16K ... 256K tokens
+        w = WORKLOADS["ulysses_128k_bf16"]
+        res = {"workload": name}
+        for n in (16384, 32768, 65536, 131072, 262144):
+            q, k, v = draw([(1, w.hq, n, w.d)] * 3, 20 + n // 16384, torch.bfloat16)
+            q, k, v = q.to(dev), k.to(dev), v.to(dev)
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+            ms_n = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=0, out=out, lse=lse),
+                         max(2, reps * 131072 // n // 4))
+            fl_n = 4.0 * w.d * w.hq * pairs(n, n, 0)
+            res[f"{n // 1024}k_ms"] = round(ms_n, 3)
+            res[f"{n // 1024}k_TFLOP/s"] = round(fl_n / ms_n / 1e9, 1)
+            del q, k, v, out, lse
+        return res
     elif name == "longnet_32k_bf16":
         q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
@@ -290,6 +314,9 @@ def run(name, reps):
         raise ValueError(name)
     res = {"workload": name, "ms": round(ms, 3), "TFLOP/s": round(fl / ms / 1e9, 1),
            "frac_peak": round(fl / ms / 1e9 / PEAK_TFLOPS, 3), "flop": fl}
+    if name == "ulysses_128k_bf16":
+        res.update({"segments_8x16k_ms": round(ms_s, 3),
+                    "segments_8x16k_TFLOP/s": round(fl / ms_s / 1e9, 1)})
     if name.startswith("ring_16k"):
         # `ms`: the driver's default stream lanes; the other count for comparison
         res.update({"alt_lanes": alt, "alt_lanes_ms": round(ms1, 3),
@@ -307,7 +334,8 @@ def main():
     ap.add_argument("--workload", nargs="*",
                     default=["ulysses_128k_bf16", "ring_16k_bf16", "ring_16k_bf16_zigzag",
                              "longnet_32k_bf16", "longnet_page_32k_bf16",
-                             "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge"])
+                             "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge",
+                             "ulysses_len_sweep"])
     ap.add_argument("--reps", type=int, default=10)
     args = ap.parse_args()
     print(json.dumps({"kernel_sources_sha256_16": source_hashes(),

@@ -327,19 +327,27 @@ def test_zigzag_ring_16k_full_size_full_oracle():
 
 def test_ulysses_128k_full_size_sampled():
     """4 heads, d=128, 131072 tokens, causal, one call in the launch
-    configuration bench.py times (bf16 O, fp32 LSE).  O and LSE start as
-    NaN and every row must come back finite (each query sees at least its
-    own key); then one seeded row in every 32-row slice (one wave's rows of
-    one query tile) of every head, 4096 rows per head with rows 0 and N-1,
-    against the oracle (0.55 TFLOP fp64: about 6 s on 16 host cores)."""
+    configuration bench.py times (bf16 O, fp32 LSE), and the same input as 8
+    KV segments of 16384 swept through the fused merge into an fp32
+    accumulator.  O and LSE start as NaN and every row must come back finite
+    (each query sees at least its own key); then one seeded row in every
+    32-row slice (one wave's rows of one query tile) of every head, 4096 rows
+    per head with rows 0 and N-1, against the oracle (0.55 TFLOP fp64: about
+    6 s on 16 host cores, shared by both checks)."""
     w = WORKLOADS["ulysses_128k_bf16"]
     q, k, v = workload_inputs(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device=DEV)
-    sa.attn_segment_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal_offset=0, out=out, lse=lse)
+    sa.attn_segment_fwd(qd, kd, vd, causal_offset=0, out=out, lse=lse)
+    seg_out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    seg_lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device=DEV)
+    emulate.sweep_fwd(qd, kd, vd, 8, 0, True, seg_out, seg_lse)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all(), "unwritten or non-finite O rows"
-    assert torch.isfinite(lse).all(), "unwritten or non-finite LSE rows"
+    del qd, kd, vd
+    for o_, l_, what in ((out, lse, "one call"), (seg_out, seg_lse, "8 segments")):
+        assert torch.isfinite(o_).all(), f"{what}: unwritten or non-finite O rows"
+        assert torch.isfinite(l_).all(), f"{what}: unwritten or non-finite LSE rows"
     rows = []
     for h in range(w.hq):
         rows += [h * w.nq + i for i in
@@ -350,24 +358,32 @@ def test_ulysses_128k_full_size_sampled():
     lg = to_np(lse).reshape(-1)[rows]
     assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // w.nq,
                   what="ulysses 128k")
+    og = to_np(seg_out).reshape(-1, w.d)[rows]
+    lg = to_np(seg_lse).reshape(-1)[rows]
+    assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // w.nq,
+                  what="ulysses 128k as 8 KV segments")
 
 
 LONG_CASES = [
-    # (hq, hkv, nq, nk, delta, out dtype)
-    (2, 1, 16384 + 77, 16384 + 77, 0, torch.bfloat16),       # causal, ragged last tile
-    (2, 2, 16384 + 300, 20000, -700, torch.float32),          # early rows see no key
-    (3, 1, 17000, 5000, None, torch.bfloat16),                # non-causal, ragged key tail
-    (1, 1, 16384, 16384 + 999, 999, torch.float32),           # keys ahead of the queries
+    # (hq, hkv, nq, nk, delta, out dtype); 24 query heads give the 384-row
+    # shape its four workgroups per CU, fewer heads take the 256-row shape
+    (24, 8, 16384 + 77, 16384 + 77, 0, torch.bfloat16),      # causal, ragged last tile
+    (24, 24, 16384 + 300, 20000, -700, torch.float32),        # early rows see no key
+    (24, 4, 17000, 5000, None, torch.bfloat16),               # non-causal, ragged key tail
+    (24, 1, 16384, 16384 + 999, 999, torch.float32),          # keys ahead of the queries
+    (2, 1, 16384 + 77, 16384 + 77, 0, torch.bfloat16),
+    (3, 1, 17000, 5000, None, torch.bfloat16),
 ]
 
 
 @pytest.mark.parametrize("hq,hkv,nq,nk,delta,odt", LONG_CASES)
 def test_long_call_shape(hq, hkv, nq, nk, delta, odt):
     """Long d = 128 calls that write their own output (at least 16384 query
-    rows) run with 384-row workgroups.  O and LSE start as NaN; every O row
-    must come back finite, every LSE row finite or -inf exactly where the
-    oracle says the row sees no key; one seeded row in every 32-row slice of
-    every head against the oracle."""
+    rows, and enough query tiles for four workgroups per CU) run with 384-row
+    workgroups; with fewer heads the same lengths take 256-row workgroups.
+    O and LSE start as NaN; every O row must come back finite, every LSE row
+    finite or -inf exactly where the oracle says the row sees no key; one
+    seeded row in every 32-row slice of every head against the oracle."""
     d = 128
     q, k, v = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d)], 1400 + nq + hq)
     out = torch.full(q.shape, float("nan"), dtype=odt, device=DEV)
