@@ -124,7 +124,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the multi-GPU "
+        print(json.dumps({"error": "seqattn runs on one GPU only: the multi-GPU "
                                    "collectives (all-to-all, ring exchange) are not built; "
                                    "run with --gpus 1"}))
         sys.exit(2)

@@ -59,7 +59,7 @@ typedef enum {
     SEQATTN_ERR_SHAPE = -3,       /* shapes inconsistent or out of range */
     SEQATTN_ERR_STRIDE = -4,      /* stride/alignment rule broken */
     SEQATTN_ERR_ALIAS = -5,       /* an output overlaps an input */
-    SEQATTN_ERR_UNSUPPORTED = -6, /* valid request this build does not serve */
+    SEQATTN_ERR_UNSUPPORTED = -6, /* valid request the library does not serve */
     SEQATTN_ERR_WORKSPACE = -7,   /* workspace missing or too small */
     SEQATTN_ERR_HIP = -8          /* HIP launch/runtime error */
 } seqattn_status;

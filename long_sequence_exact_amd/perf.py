@@ -318,7 +318,7 @@ def run(name, reps):
         res.update({"segments_8x16k_ms": round(ms_s, 3),
                     "segments_8x16k_TFLOP/s": round(fl / ms_s / 1e9, 1)})
     if name.startswith("ring_16k"):
-        # `ms`: the driver's default stream lanes; the other count for comparison
+        # `ms`: the ring function's default stream lanes; the other count for comparison
         res.update({"alt_lanes": alt, "alt_lanes_ms": round(ms1, 3),
                     "alt_lanes_TFLOP/s": round(fl / ms1 / 1e9, 1)})
     if name.startswith("ring_16k"):
