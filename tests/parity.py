@@ -14,15 +14,18 @@ ref| / max|ref|): a causal row deep in the sequence averages many keys and is
 small, so a whole run of wrong late rows can stay under the normwise bound,
 never under the per-row one.
 
-dK and dV rows are measured the same way.  dQ rows take a higher floor,
-DQ_FLOOR times the largest |dQ| of the head: dQ_i is sigma sum_j P_ij (dP_ij
-- D_i) k_j, and where one key holds nearly all of a row's softmax weight the
-bracket is a difference of nearly equal terms, so dQ_i is tiny while its
+dV rows are measured the same way.  dQ and dK rows take a higher floor,
+DS_FLOOR times the largest |dQ| or |dK| of the head.  Both are sums over
+dS_ij = P_ij (dP_ij - D_i): dQ_i = sigma sum_j dS_ij k_j and dK_j = sigma
+sum_i dS_ij q_i.  Where one key holds nearly all of a query's softmax weight
+the bracket is a difference of nearly equal terms, so dQ_i, and dK_j of a
+key whose gradient comes from such queries (a causal key near the start of
+a dilated segment, or a key seen by only a few queries), is tiny while its
 absolute error is not.  That error comes from D_i = dO_i . O_i, whose O was
-formed with P rounded to bf16 in the forward; it is bounded by a small
-fraction of the head's dQ scale, not of the row's own value (a row with two
-keys of weights 1 - e and e has dQ proportional to e and an error about
-2^-9 of the row's scale).
+formed with P rounded to bf16 in the forward, and from dS rounded to bf16
+before its product; it is bounded by a small fraction of the head's scale,
+not of the row's own value (a query row with two keys of weights 1 - e and e
+has dQ proportional to e and an error about 2^-9 of the row's scale).
 
 Element-wise relative error is unbounded where an output crosses zero; its
 regularised form |x - ref| / (|ref| + 1e-3 max|ref|) is reported beside the
@@ -40,7 +43,7 @@ import torch
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 LSE_TOL = 1e-3
 ROW_FLOOR = 1e-3
-DQ_FLOOR = 0.25
+DS_FLOOR = 0.25
 
 
 def to_np(t):
@@ -110,9 +113,9 @@ def _test_name():
 def check_close(x, ref, tol, heads=None, what="", name="o", floor=None):
     """Assert x (array or tensor) matches ref within tol by the per-row
     measure, with no NaN; the message carries all three measures.  floor
-    defaults to DQ_FLOOR for a tensor named dq, else ROW_FLOOR."""
+    defaults to DS_FLOOR for a tensor named dq or dk, else ROW_FLOOR."""
     if floor is None:
-        floor = DQ_FLOOR if name == "dq" else ROW_FLOOR
+        floor = DS_FLOOR if name in ("dq", "dk") else ROW_FLOOR
     if isinstance(x, torch.Tensor):
         assert not torch.isnan(x).any(), f"{what}: NaN in {name}"
         x = to_np(x)

@@ -5,8 +5,12 @@ attention (forward and backward, with and without head-dependent offsets),
 batch 1 or 2.
 
 Each case prints its parameters in the assertion message, so a failure names
-the case; the draw is deterministic (numpy generator, fixed seed).
+the case; the draw is deterministic (numpy generator, fixed seed).  The
+environment variable SEQATTN_FUZZ_SCALE multiplies the number of cases (the
+first cases of a longer draw are the default ones).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +22,7 @@ from tests.parity import TOL, assert_parity, check_close, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+SCALE = max(1, int(os.environ.get("SEQATTN_FUZZ_SCALE", "1")))
 
 
 def _np32(t):
@@ -51,7 +56,7 @@ def _fwd_cases(count, seed):
     return out
 
 
-@pytest.mark.parametrize("case", _fwd_cases(40, 20261203), ids=lambda c: f"fwd{c[0]}")
+@pytest.mark.parametrize("case", _fwd_cases(40 * SCALE, 20261203), ids=lambda c: f"fwd{c[0]}")
 def test_fuzz_segment_fwd(case):
     i, d, hkv, group, nq, nk, delta, dtype, split, out_bf16, seq_major, bsz = case
     hq = hkv * group
@@ -94,7 +99,7 @@ def _bwd_cases(count, seed):
     return out
 
 
-@pytest.mark.parametrize("case", _bwd_cases(20, 20261204), ids=lambda c: f"bwd{c[0]}")
+@pytest.mark.parametrize("case", _bwd_cases(20 * SCALE, 20261204), ids=lambda c: f"bwd{c[0]}")
 def test_fuzz_segment_bwd(case):
     i, d, hkv, group, nq, nk, delta, grads_bf16, seq_major, bsz = case
     hq = hkv * group
@@ -130,7 +135,7 @@ def _dilated_cases(count, seed):
     return out
 
 
-@pytest.mark.parametrize("case", _dilated_cases(16, 20261205), ids=lambda c: f"dil{c[0]}")
+@pytest.mark.parametrize("case", _dilated_cases(16 * SCALE, 20261205), ids=lambda c: f"dil{c[0]}")
 def test_fuzz_dilated(case):
     i, d, hkv, group, n, ws, rs, causal, head_shift, bsz = case
     hq = hkv * group

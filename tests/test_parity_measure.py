@@ -10,7 +10,9 @@ import torch
 
 import oracle
 from long_sequence_exact_amd.synth import draw, sample_rows
-from tests.parity import DQ_FLOOR, TOL, ROW_FLOOR, errors, max_rel_error
+import pytest
+
+from tests.parity import DS_FLOOR, TOL, ROW_FLOOR, check_close, errors, max_rel_error
 
 TOL_BF16 = TOL[torch.bfloat16]
 
@@ -82,14 +84,31 @@ def test_non_finite_output_is_an_infinite_error():
     assert max_rel_error(x, ref) == float("inf")
 
 
-def test_dq_floor_is_a_quarter_of_the_head_scale():
+def test_gradient_floor_is_a_quarter_of_the_head_scale():
     ref = np.ones((5, 4))
-    ref[0] = 1e-3                    # a near-one-hot row: tiny dQ
+    ref[0] = 1e-3                    # a near-one-hot row: tiny dQ (or dK)
     x = ref.copy()
     x[0] += 4e-3                     # its absolute error, far above its own size
     assert max_rel_error(x, ref) > 1.0                                  # output rule
-    assert abs(max_rel_error(x, ref, floor=DQ_FLOOR) - 4e-3 / DQ_FLOOR) < 1e-12
-    # a wrong typical row still fails under the dQ rule
+    assert abs(max_rel_error(x, ref, floor=DS_FLOOR) - 4e-3 / DS_FLOOR) < 1e-12
+    # a wrong typical row still fails under the gradient rule
     x = ref.copy()
     x[3] *= 0.9
-    assert max_rel_error(x, ref, floor=DQ_FLOOR) > 4 * TOL_BF16
+    assert max_rel_error(x, ref, floor=DS_FLOOR) > 4 * TOL_BF16
+
+
+def test_check_close_takes_the_gradient_floor_for_dq_and_dk_only():
+    ref = np.ones((5, 4))
+    ref[0] = 1e-3
+    x = ref.copy()
+    x[0] += 4e-3
+    for name in ("dq", "dk"):
+        check_close(x, ref, TOL_BF16, name=name)
+    for name in ("dv", "o"):
+        with pytest.raises(AssertionError):
+            check_close(x, ref, TOL_BF16, name=name)
+    x = ref.copy()
+    x[3] *= 0.9                      # a wrong typical row fails for every tensor
+    for name in ("dq", "dk", "dv", "o"):
+        with pytest.raises(AssertionError):
+            check_close(x, ref, TOL_BF16, name=name)
