@@ -314,3 +314,67 @@ def test_bwd_noalloc_validation_errors(L):
             r(dob), 0, 0.0, 0, r(dqb), r(T(dk.data, _lib.F32, 1, kb.h, 512, 128)),
             r(T(dv.data, _lib.F32, 1, kb.h, 512, 128)), None) == EWS
         assert "scratch" in L.seqattn_last_error().decode()
+
+
+C_PROGRAM = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include <string.h>
+#include "seqattn.h"
+
+/* A plain C caller: the descriptor layout it sees, and calls whose arguments
+   are rejected before any HIP call (fake device addresses, never touched). */
+int main(void)
+{
+    printf("size %zu data %zu dtype %zu b %zu d %zu stride_n %zu\n", sizeof(seqattn_tensor),
+           offsetof(seqattn_tensor, data), offsetof(seqattn_tensor, dtype),
+           offsetof(seqattn_tensor, b), offsetof(seqattn_tensor, d),
+           offsetof(seqattn_tensor, stride_n));
+    printf("version %d\n", seqattn_version());
+    seqattn_tensor q = {(void *)0x7f0000000000ull, SEQATTN_BF16, 1, 4, 256, 128,
+                        4 * 256 * 128, 256 * 128, 128};
+    seqattn_tensor k = q, v = q, o = q, lse = q;
+    k.data = (void *)0x7f0040000000ull;
+    v.data = (void *)0x7f0080000000ull;
+    o.data = (void *)0x7f00c0000000ull;
+    lse.data = (void *)0x7f0100000000ull;
+    lse.dtype = SEQATTN_F32;
+    lse.d = 1;
+    lse.stride_b = 4 * 256;
+    lse.stride_h = 256;
+    lse.stride_n = 1;
+    int st = seqattn_attn_segment_fwd(NULL, &k, &v, 0, 0.f, 0, &o, &lse, NULL);
+    printf("null %d %s | %s\n", st, seqattn_status_string(st), seqattn_last_error());
+    k.d = 64;
+    st = seqattn_attn_segment_fwd(&q, &k, &v, 0, 0.f, 0, &o, &lse, NULL);
+    printf("shape %d %s\n", st, seqattn_status_string(st));
+    k.d = 128;
+    o.data = q.data;
+    st = seqattn_attn_segment_fwd(&q, &k, &v, 0, 0.f, 0, &o, &lse, NULL);
+    printf("alias %d %s\n", st, seqattn_status_string(st));
+    return 0;
+}
+"""
+
+
+def test_plain_c_caller(L, tmp_path):
+    """The header compiles as C99 with warnings as errors, a C program links
+    against the library, sees the same descriptor layout as the binding, and
+    gets the documented error codes back."""
+    src = tmp_path / "caller.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), str(src), "-o", str(exe), "-L", libdir,
+                    "-lseqattn", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    lines = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    f = _lib.Tensor
+    assert lines["size"] == (f"{ctypes.sizeof(f)} data {f.data.offset} dtype {f.dtype.offset} "
+                             f"b {f.b.offset} d {f.d.offset} stride_n {f.stride_n.offset}")
+    assert lines["version"] == "100"
+    assert lines["null"].startswith(f"{ENULL} ")
+    assert lines["null"].split(" | ")[1]          # the detail message is set
+    assert lines["shape"].startswith(f"{ESHAPE} ")
+    assert lines["alias"].startswith(f"{EALIAS} ")
