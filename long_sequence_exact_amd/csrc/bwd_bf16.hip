@@ -292,13 +292,13 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
         }
         if (tid < BQ) {
             const int i = q0 + tid;
-            lreg = INFINITY;  // +inf: the row contributes P = 0
+            // raw values: the stage formats them a step later, so no wait
+            // for these loads (or the tile loads before them) falls here
+            lreg = -INFINITY;  // a row past the end contributes P = 0
             dreg = 0.f;
             if (i < Nq) {
-                const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
-                                   h * p.lse.sh + sl + (int64_t)i * p.lse.sn);
-                if (lv != -INFINITY)
-                    lreg = lv * kLog2e;
+                lreg = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
+                         h * p.lse.sh + sl + (int64_t)i * p.lse.sn);
                 dreg = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss +
                          h * p.dvec.sh + sd + (int64_t)i * p.dvec.sn);
             }
@@ -311,7 +311,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             *(u32x4 *)(dOs + buf * TB + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
         }
         if (tid < BQ) {
-            lse2s[buf][tid] = lreg;
+            // LSE in log2 units; -inf (no visible key) becomes +inf: P = 0
+            lse2s[buf][tid] = lreg == -INFINITY ? INFINITY : lreg * kLog2e;
             Dsh[buf][tid] = -dreg;  // -D: the dP accumulators start from it
         }
     };
@@ -595,13 +596,12 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
         }
         if (tid < BQ) {
             const int i = q0 + tid;
-            lreg = INFINITY;
+            // raw values, formatted when staged
+            lreg = -INFINITY;
             dreg = 0.f;
             if (i < Nq) {
-                const float lv = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
-                                   h * p.lse.sh + sl + (int64_t)i * p.lse.sn);
-                if (lv != -INFINITY)
-                    lreg = lv * kLog2e;
+                lreg = *((const float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss +
+                         h * p.lse.sh + sl + (int64_t)i * p.lse.sn);
                 dreg = *((const float *)p.dvec.ptr + b * p.dvec.sb + s * p.dvec.ss +
                          h * p.dvec.sh + sd + (int64_t)i * p.dvec.sn);
             }
@@ -623,7 +623,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
             *(u32x4 *)(dOs + swz_off<D>(srow[u], scol[u] >> 3)) = oreg[u];
         }
         if (tid < BQ) {
-            lse2s[tid] = lreg;
+            lse2s[tid] = lreg == -INFINITY ? INFINITY : lreg * kLog2e;
             Dsh[tid] = -dreg;  // -D: the dP accumulators start from it
         }
         __syncthreads();
