@@ -470,6 +470,15 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
     const float f = is_dk ? p.scale : 1.f;
     const int64_t krow = b * out.sb + s * out.ss + g * out.sh +
                          head_shift_elems(out, p.hs_r, hr.off) + (int64_t)key * out.sn;
+    // accumulated output: every running sum read before any is written
+    float4 old[D / 32][4];
+    if (p.acc_kv) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+                old[i][gq] = *(const float4 *)((const float *)out.ptr + krow + i * 32 + gq * 8 + hl * 4);
+    }
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -478,10 +487,9 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(const BwdParams p)
             const float x0 = acc[i][gq * 4 + 0] * f, x1 = acc[i][gq * 4 + 1] * f;
             const float x2 = acc[i][gq * 4 + 2] * f, x3 = acc[i][gq * 4 + 3] * f;
             if (p.acc_kv) {  // fp32, accumulated
-                float4 *dst = (float4 *)((float *)out.ptr + krow + d0);
-                float4 w = *dst;
+                float4 w = old[i][gq];
                 w.x += x0; w.y += x1; w.z += x2; w.w += x3;
-                *dst = w;
+                *(float4 *)((float *)out.ptr + krow + d0) = w;
             } else if (out_f32) {
                 float4 w = {x0, x1, x2, x3};
                 *(float4 *)((float *)out.ptr + krow + d0) = w;
@@ -730,6 +738,23 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
 
     if (key >= Nk)
         return;
+    // accumulated outputs: every running sum is read before any is written,
+    // so the reads' round trips overlap instead of following each other
+    float4 old[2][D / 32][4];
+    if (p.acc_kv) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const View &out = which ? p.dk : p.dv;
+            const int64_t krow = b * out.sb + s * out.ss + g * out.sh +
+                                 head_shift_elems(out, p.hs_r, hr.off) + (int64_t)key * out.sn;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    old[which][i][gq] =
+                        *(const float4 *)((const float *)out.ptr + krow + i * 32 + gq * 8 + hl * 4);
+        }
+    }
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const View &out = which ? p.dk : p.dv;
@@ -746,10 +771,9 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams &p, unsigned blk)
                 const float x0 = a[gq * 4 + 0] * f, x1 = a[gq * 4 + 1] * f;
                 const float x2 = a[gq * 4 + 2] * f, x3 = a[gq * 4 + 3] * f;
                 if (p.acc_kv) {
-                    float4 *dst = (float4 *)((float *)out.ptr + krow + d0);
-                    float4 w = *dst;
+                    float4 w = old[which][i][gq];
                     w.x += x0; w.y += x1; w.z += x2; w.w += x3;
-                    *dst = w;
+                    *(float4 *)((float *)out.ptr + krow + d0) = w;
                 } else if (out_f32) {
                     float4 w = {x0, x1, x2, x3};
                     *(float4 *)((float *)out.ptr + krow + d0) = w;
@@ -976,12 +1000,19 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p, unsigned blk)
         return;
     float *dQ = (float *)p.dq.ptr + b * p.dq.sb + s * p.dq.ss + h * p.dq.sh +
                 head_shift_elems(p.dq, p.hs_r, hr.off) + (int64_t)qrow * p.dq.sn;
+    // every running sum read before any is written (overlapping round trips)
+    float4 old[D / 32][4];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+            old[i][gq] = *(const float4 *)(dQ + i * 32 + gq * 8 + hl * 4);
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int d0 = i * 32 + gq * 8 + hl * 4;
-            float4 x = *(float4 *)(dQ + d0);
+            float4 x = old[i][gq];
             x.x += p.scale * acc[i][gq * 4 + 0];
             x.y += p.scale * acc[i][gq * 4 + 1];
             x.z += p.scale * acc[i][gq * 4 + 2];

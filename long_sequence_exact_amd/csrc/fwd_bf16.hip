@@ -512,21 +512,29 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
         return;
     }
 
-    // fused merge with the running fp32 partial (o, lse)
+    // fused merge with the running fp32 partial (o, lse): its LSE and every
+    // row chunk are read before anything is written, so the reads' round
+    // trips overlap
+    float *Op = (float *)p.o.ptr + orow;
     const float la = *Lp;
+    float4 old[D / 32][4];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+            old[i][gq] = *(const float4 *)(Op + i * 32 + gq * 8 + hl * 4);
     const float M = fmaxf(la, lse_new);
     if (M == -INFINITY)
         return;  // both empty: stays (0, -inf)
     const float wa = __expf(la - M), wb = __expf(lse_new - M);
     const float tot = wa + wb;
     const float fa = wa / tot, fb = wb / tot * inv;
-    float *Op = (float *)p.o.ptr + orow;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int d0 = i * 32 + gq * 8 + hl * 4;
-            float4 a = *(float4 *)(Op + d0);
+            float4 a = old[i][gq];
             a.x = fa * a.x + fb * oacc[i][gq * 4 + 0];
             a.y = fa * a.y + fb * oacc[i][gq * 4 + 1];
             a.z = fa * a.z + fb * oacc[i][gq * 4 + 2];
