@@ -48,21 +48,25 @@ def test_segment_attention_backward(hq, hkv, nq, nk, d, delta):
         assert torch.equal(x, y.to(torch.bfloat16))
 
 
-def test_dilated_attention_backward():
+@pytest.mark.parametrize("head_shift", [False, True])
+def test_dilated_attention_backward(head_shift):
     """The same for dilated attention (causal, three branches, grouped KV
-    heads); its output is the fp32 merge accumulator, so dO = w in fp32 is
-    rounded to bf16 on the way into the backward."""
+    heads, with and without head-dependent offsets); its output is the fp32
+    merge accumulator, so dO = w in fp32 is rounded to bf16 on the way into
+    the backward."""
     hq, hkv, n, d = 4, 2, 700, 64
     ws, rs = (128, 256, 512), (1, 2, 4)
     q, k, v, w = draw([(1, hq, n, d), (1, hkv, n, d), (1, hkv, n, d), (1, hq, n, d)], 41)
     qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
     wd = w.to(DEV)
-    o = dilated_attention(qd, kd, vd, ws, rs, causal=True)
+    o = dilated_attention(qd, kd, vd, ws, rs, causal=True, head_shift=head_shift)
     assert o.dtype == torch.float32
     (o * wd.float()).sum().backward()
     torch.cuda.synchronize()
-    o_ref, _ = oracle.dilated_fwd(_np32(q), _np32(k), _np32(v), ws, rs, causal=True)
+    o_ref, _ = oracle.dilated_fwd(_np32(q), _np32(k), _np32(v), ws, rs, causal=True,
+                                  head_shift=head_shift)
     check_close(o.detach(), o_ref, BTOL, what="autograd dilated", name="o")
-    ref = oracle.dilated_bwd(_np32(q), _np32(k), _np32(v), _np32(w), ws, rs, causal=True)
+    ref = oracle.dilated_bwd(_np32(q), _np32(k), _np32(v), _np32(w), ws, rs, causal=True,
+                             head_shift=head_shift)
     for name, x, r in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
         check_close(x, r, BTOL, what="autograd dilated", name=name)
