@@ -16,8 +16,8 @@
 //     VALU work can overlap another's MFMAs.  Two other shapes: a long
 //     d = 128 call that writes its own output, with enough query tiles for
 //     four workgroups per CU, takes 12 waves (384 rows, three per SIMD) with
-//     64-key tiles, and a d = 64 launch too small to fill the chip takes 4
-//     waves (128 rows, four workgroups per CU);
+//     64-key tiles, and a causal d = 64 launch, or one too small to fill
+//     the chip, takes 4 waves (128 rows, four workgroups per CU);
 //   * the workgroup walks the KV segment in tiles of 128 keys (64 at
 //     d = 64), double-buffered in LDS and filled by direct HBM -> LDS buffer
 //     loads (rows past the segment end read as zeros), so staging costs no
@@ -584,10 +584,13 @@ hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
     }
     // d = 64 launches (LongNet's branches) take 64-key tiles at four waves
     // per SIMD: two 8-wave workgroups per CU, so an XCD runs twice as many
-    // at once.  A launch with fewer workgroups than the chip holds (a
-    // long-segment branch selects few rows) takes 4-wave workgroups of 128
-    // rows instead, four per CU, so its rows spread over twice as many CUs
-    const bool small = (int64_t)nqt * BH < 2 * 256;
+    // at once.  A causal launch, or one with fewer workgroups than the chip
+    // holds (a long-segment branch selects few rows), takes 4-wave
+    // workgroups of 128 rows instead, four per CU: their rows spread over
+    // twice as many CUs, and the causal triangle is cut into finer tiles
+    // (LongNet's causal page mixture 0.436 against 0.450 ms; the non-causal
+    // 32K mixture keeps the 8-wave tiles, 0.622 against 0.627)
+    const bool small = (int64_t)nqt * BH < 2 * 256 || !p.noncausal;
     if (small) {
         nqt = (p.Nq + 127) / 128;
         p.grouped = use_grouped(nqt, BH, 4 * kXcdCUs);
