@@ -19,13 +19,12 @@ from . import attn_segment_bwd, attn_segment_fwd, dilated_attn_bwd, dilated_attn
 __all__ = ["segment_attention", "dilated_attention"]
 
 
-def _grad_in(d_o, like):
-    """The upstream gradient as the kernels take it: bf16, d contiguous."""
+def _grad_in(d_o):
+    """The upstream gradient as the kernels take it: bf16 and contiguous (so
+    its rows are 16-byte aligned)."""
     if d_o.dtype != torch.bfloat16:
         d_o = d_o.to(torch.bfloat16)
-    if d_o.stride(-1) != 1 or d_o.data_ptr() % 16:
-        d_o = d_o.contiguous()
-    return d_o
+    return d_o.contiguous()
 
 
 class _SegmentAttention(torch.autograd.Function):
@@ -39,7 +38,7 @@ class _SegmentAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, d_o):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = attn_segment_bwd(q, k, v, o, lse, _grad_in(d_o, q),
+        dq, dk, dv = attn_segment_bwd(q, k, v, o, lse, _grad_in(d_o),
                                       causal_offset=ctx.causal_offset, scale=ctx.scale)
         return dq, dk, dv, None, None
 
@@ -57,7 +56,7 @@ class _DilatedAttention(torch.autograd.Function):
     def backward(ctx, d_o):
         q, k, v, o, lse = ctx.saved_tensors
         ws, rs, causal, scale, head_shift = ctx.args
-        dq, dk, dv = dilated_attn_bwd(q, k, v, o, lse, _grad_in(d_o, q), ws, rs,
+        dq, dk, dv = dilated_attn_bwd(q, k, v, o, lse, _grad_in(d_o), ws, rs,
                                       causal=causal, scale=scale, head_shift=head_shift)
         return dq, dk, dv, None, None, None, None, None
 
