@@ -207,7 +207,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_counters(),
                      "mfma_busy": mfma_busy_from_counters(),
-                     "kernel": "fwd_bf16_kernel<128, 64, 12>",
+                     "kernel": "fwd_bf16_kernel<128, 64, 12, false>",
                      "avg_launch_ms": round(avg_launch_ms, 4)},
         "cpu_baseline": cpu,
     }

@@ -123,6 +123,31 @@ int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
                              void *hip_stream);
 
 /*
+ * seqattn_attn_segment_fwd_ws -- seqattn_attn_segment_fwd with a caller-owned
+ * workspace, for calls too short to fill the GPU: when the query block's
+ * 256-row tiles are fewer than the GPU's 256 compute units (bf16, d = 128, at
+ * least 1024 keys, no SEQATTN_ACCUMULATE), each tile's keys are cut into 2-8
+ * chunks of at least 512 keys (about one work item per compute unit in all)
+ * computed by separate workgroups, whose fp32 partials (O, LSE) go to
+ * the workspace and are then merged by their log-sum-exp into o and lse
+ * ("Ultra-Long Sequence Distributed Transformer", Abstract: partial
+ * attention per segment, combined exactly).  The result equals the unsplit
+ * call's up to rounding order; a call the rule does not split runs exactly
+ * as seqattn_attn_segment_fwd.
+ *
+ * workspace: seqattn_workspace_size(SEQATTN_OP_SEGMENT_FWD, q, k, 0) bytes,
+ * 16-byte aligned device memory overlapping no tensor of the call (NULL when
+ * that size is 0).  Errors: as seqattn_attn_segment_fwd, plus WORKSPACE
+ * (missing, too small or misaligned when the call is split) and ALIAS (the
+ * workspace overlaps a tensor).
+ */
+int seqattn_attn_segment_fwd_ws(const seqattn_tensor *q, const seqattn_tensor *k,
+                                const seqattn_tensor *v, int64_t causal_offset,
+                                float softmax_scale, uint32_t flags, seqattn_tensor *o,
+                                seqattn_tensor *lse, void *workspace, size_t workspace_bytes,
+                                void *hip_stream);
+
+/*
  * seqattn_lse_merge -- in place acc <- merge(acc, b), row by row:
  *   M = max(La, Lb), wa = exp(La - M), wb = exp(Lb - M),
  *   O = (wa Oa + wb Ob) / (wa + wb), L = M + log(wa + wb);

@@ -34,12 +34,15 @@ def _lse_shape(q):
 
 
 def attn_segment_fwd(q, k, v, causal_offset=None, scale=None, out=None, lse=None,
-                     accumulate=False, out_dtype=None):
+                     accumulate=False, out_dtype=None, workspace=None, split=True):
     """Partial attention of q against one KV segment.
 
     causal_offset: None (non-causal) or delta = q_start - k_start; key j is
     visible to query i iff j <= i + delta.  With accumulate=True, ``out``
     (fp32) and ``lse`` hold a running partial that receives the merge.
+    A call too short to fill the GPU splits its key range over more
+    workgroups (seqattn_attn_segment_fwd_ws); its workspace is allocated
+    here unless given.  split=False runs seqattn_attn_segment_fwd instead.
     """
     L = _lib.lib()
     if out is None:
@@ -52,10 +55,25 @@ def attn_segment_fwd(q, k, v, causal_offset=None, scale=None, out=None, lse=None
     delta = NONCAUSAL if causal_offset is None else int(causal_offset)
     dq, dk, dv = _lib.desc(q), _lib.desc(k), _lib.desc(v)
     do_, dl = _lib.desc(out), _lib.desc(lse, lse=True)
-    _lib.check(L.seqattn_attn_segment_fwd(
+    if not split:
+        _lib.check(L.seqattn_attn_segment_fwd(
+            ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), delta,
+            float(scale or 0.0), ACCUMULATE if accumulate else 0,
+            ctypes.byref(do_), ctypes.byref(dl), ctypes.c_void_p(_lib.stream_handle())))
+        return out, lse
+    need = 0 if accumulate else int(L.seqattn_workspace_size(
+        _lib.OP_SEGMENT_FWD, ctypes.byref(dq), ctypes.byref(dk), 0))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must be on the GPU")
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(L.seqattn_attn_segment_fwd_ws(
         ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), delta,
         float(scale or 0.0), ACCUMULATE if accumulate else 0,
-        ctypes.byref(do_), ctypes.byref(dl), ctypes.c_void_p(_lib.stream_handle())))
+        ctypes.byref(do_), ctypes.byref(dl), ctypes.c_void_p(wptr), wbytes,
+        ctypes.c_void_p(_lib.stream_handle())))
     return out, lse
 
 

@@ -22,7 +22,8 @@ CAUSAL = 2
 HEAD_SHIFT = 4
 OP_SEGMENT_FWD, OP_LSE_MERGE, OP_DILATED_FWD, OP_SEGMENT_BWD, OP_DILATED_BWD = 0, 1, 2, 3, 4
 
-EXPORTS = ("seqattn_attn_segment_fwd", "seqattn_lse_merge", "seqattn_dilated_attn_fwd",
+EXPORTS = ("seqattn_attn_segment_fwd", "seqattn_attn_segment_fwd_ws", "seqattn_lse_merge",
+           "seqattn_dilated_attn_fwd",
            "seqattn_attn_segment_bwd", "seqattn_attn_segment_bwd_noalloc",
            "seqattn_dilated_attn_bwd", "seqattn_head_relayout",
            "seqattn_workspace_size", "seqattn_status_string", "seqattn_last_error",
@@ -57,6 +58,8 @@ def lib():
     P = ctypes.POINTER(Tensor)
     I64, F, U32, VP = ctypes.c_int64, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p
     L.seqattn_attn_segment_fwd.argtypes = [P, P, P, I64, F, U32, P, P, VP]
+    L.seqattn_attn_segment_fwd_ws.argtypes = [P, P, P, I64, F, U32, P, P, VP, ctypes.c_size_t,
+                                              VP]
     L.seqattn_lse_merge.argtypes = [P, P, P, P, VP]
     L.seqattn_dilated_attn_fwd.argtypes = [P, P, P, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                            ctypes.c_int32, F, U32, P, P, VP, ctypes.c_size_t,
@@ -73,10 +76,10 @@ def lib():
     L.seqattn_status_string.restype = ctypes.c_char_p
     L.seqattn_status_string.argtypes = [ctypes.c_int]
     L.seqattn_last_error.restype = ctypes.c_char_p
-    for f in ("seqattn_attn_segment_fwd", "seqattn_lse_merge", "seqattn_dilated_attn_fwd",
-              "seqattn_attn_segment_bwd", "seqattn_attn_segment_bwd_noalloc",
-           "seqattn_dilated_attn_bwd", "seqattn_head_relayout",
-              "seqattn_version"):
+    for f in ("seqattn_attn_segment_fwd", "seqattn_attn_segment_fwd_ws", "seqattn_lse_merge",
+              "seqattn_dilated_attn_fwd", "seqattn_attn_segment_bwd",
+              "seqattn_attn_segment_bwd_noalloc", "seqattn_dilated_attn_bwd",
+              "seqattn_head_relayout", "seqattn_version"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

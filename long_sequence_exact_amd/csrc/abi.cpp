@@ -45,6 +45,7 @@ int64_t numel(const seqattn_tensor *t) { return t->b * t->h * t->n * t->d; }
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 constexpr int64_t kMaxBH = (int64_t)1 << 20;
 constexpr int64_t kMaxStride = (int64_t)1 << 40;  // elements; keeps every extent in int64
+constexpr int64_t kSplitCUs = 256;  // compute units of the GPU (a key-range split below one tile per CU)
 
 // Structural checks of one descriptor: non-null, known dtype, non-negative
 // dims within range, non-negative strides, 16-byte row alignment (rows, d>1).
@@ -310,34 +311,49 @@ std::vector<HeadSel> head_sels(bool shift, int64_t r, int Hq, int Hkv, bool kern
     return out;
 }
 
-}  // namespace
+// Key-range split of a segment forward whose 256-row query tiles are too
+// few to fill the chip (fewer than its compute units): each tile's keys are
+// cut into nchunk chunks of kv_chunk keys, computed by separate workgroups
+// into fp32 partials and merged by their LSE.  Decided from the shapes alone
+// (bf16, d = 128): about one work item per compute unit, chunks of at least
+// 512 keys.  Fewer, longer chunks beat more items: at 8K tokens and 4 heads
+// two chunks per tile ran 0.112 ms, four 0.127, none 0.167.
+struct SegmentSplit {
+    int nchunk = 1, kv_chunk = 0;
+};
 
-extern "C" {
-
-int seqattn_version(void) { return SEQATTN_VERSION; }
-
-const char *seqattn_status_string(int status)
+SegmentSplit segment_split(const seqattn_tensor *q, const seqattn_tensor *k)
 {
-    switch (status) {
-    case SEQATTN_OK: return "ok";
-    case SEQATTN_ERR_NULL: return "null pointer";
-    case SEQATTN_ERR_DTYPE: return "unsupported or mismatched dtype";
-    case SEQATTN_ERR_SHAPE: return "invalid shape";
-    case SEQATTN_ERR_STRIDE: return "invalid stride or alignment";
-    case SEQATTN_ERR_ALIAS: return "output aliases an input";
-    case SEQATTN_ERR_UNSUPPORTED: return "unsupported configuration";
-    case SEQATTN_ERR_WORKSPACE: return "workspace missing or too small";
-    case SEQATTN_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-    }
+    constexpr int64_t kTarget = 256;     // work items per launch aimed at (one per CU)
+    constexpr int64_t kMinChunk = 512;   // keys per chunk, at least
+    SegmentSplit sp;
+    if (!q || !k || q->dtype != SEQATTN_BF16 || q->d != 128 || k->n < 2 * kMinChunk)
+        return sp;
+    const int64_t tiles = q->b * q->h * ((q->n + 255) / 256);
+    if (tiles == 0 || tiles >= kSplitCUs)
+        return sp;
+    const int64_t want = std::min<int64_t>((kTarget + tiles - 1) / tiles, 8);
+    // chunks a multiple of 256 keys (two key tiles)
+    int64_t chunk = (k->n + want - 1) / want;
+    chunk = std::max((chunk + 255) / 256 * 256, kMinChunk);
+    sp.kv_chunk = (int)chunk;
+    sp.nchunk = (int)((k->n + chunk - 1) / chunk);
+    if (sp.nchunk < 2)
+        sp = SegmentSplit();
+    return sp;
 }
 
-const char *seqattn_last_error(void) { return g_err; }
+size_t segment_split_bytes(const seqattn_tensor *q, const SegmentSplit &sp)
+{
+    if (sp.nchunk < 2)
+        return 0;
+    return (size_t)sp.nchunk * (size_t)(q->b * q->h * q->n) * (size_t)(q->d + 1) * sizeof(float);
+}
 
-int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
-                             const seqattn_tensor *v, int64_t causal_offset,
-                             float softmax_scale, uint32_t flags, seqattn_tensor *o,
-                             seqattn_tensor *lse, void *hip_stream)
+int segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k, const seqattn_tensor *v,
+                int64_t causal_offset, float softmax_scale, uint32_t flags, seqattn_tensor *o,
+                seqattn_tensor *lse, void *workspace, size_t workspace_bytes, bool may_split,
+                void *hip_stream)
 {
     int st;
     if ((st = check_qkv(q, k, v, false)) || (st = check_out(o, lse, q, k, v)))
@@ -377,10 +393,109 @@ int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
                                             p.o_f32, stream_of(hip_stream)),
                           "fill_empty");
     }
+    const SegmentSplit sp = may_split && !acc ? segment_split(q, k) : SegmentSplit();
+    if (sp.nchunk > 1) {
+        const size_t need = segment_split_bytes(q, sp);
+        if (!workspace || workspace_bytes < need)
+            return fail(SEQATTN_ERR_WORKSPACE, "need %zu bytes of workspace", need);
+        if ((uintptr_t)workspace % 16)
+            return fail(SEQATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        const uintptr_t wl = (uintptr_t)workspace, wh = wl + need;
+        const seqattn_tensor *all[5] = {q, k, v, o, lse};
+        for (const seqattn_tensor *t : all) {
+            uintptr_t tl, th;
+            extent(t, &tl, &th);
+            if (tl != th && tl < wh && wl < th)
+                return fail(SEQATTN_ERR_ALIAS, "workspace overlaps a tensor");
+        }
+        // partials: O [nchunk][B][Hq][Nq][d], then LSE [nchunk][B][Hq][Nq], fp32
+        const int64_t bhn = (int64_t)p.B * p.Hq * p.Nq;
+        float *po = (float *)workspace;
+        float *pl = po + sp.nchunk * bhn * q->d;
+        FwdParams s = p;
+        s.o.ptr = po;
+        s.o.sb = (int64_t)p.Hq * p.Nq * q->d;
+        s.o.ss = 0;
+        s.o.sh = (int64_t)p.Nq * q->d;
+        s.o.sn = q->d;
+        s.lse.ptr = pl;
+        s.lse.sb = (int64_t)p.Hq * p.Nq;
+        s.lse.ss = 0;
+        s.lse.sh = p.Nq;
+        s.lse.sn = 1;
+        s.o_f32 = 1;
+        s.kv_chunk = sp.kv_chunk;
+        s.nchunk = sp.nchunk;
+        s.o_chunk = bhn * q->d;
+        s.l_chunk = bhn;
+        hipError_t e = launch_fwd_bf16(s, (int)q->d, stream_of(hip_stream));
+        if (e != hipSuccess)
+            return hip_status(e, "attn_segment_fwd launch");
+        ChunkMergeParams m;
+        m.o = p.o;
+        m.lse = p.lse;
+        m.po = po;
+        m.pl = pl;
+        m.B = p.B;
+        m.H = p.Hq;
+        m.N = p.Nq;
+        m.d = (int)q->d;
+        m.Nk = p.Nk;
+        m.delta = p.delta;
+        m.noncausal = p.noncausal;
+        m.tile_rows = 256;
+        m.kv_chunk = sp.kv_chunk;
+        m.nchunk = sp.nchunk;
+        m.o_f32 = p.o_f32;
+        return hip_status(launch_chunk_merge(m, stream_of(hip_stream)), "chunk merge launch");
+    }
     const hipError_t e = q->dtype == SEQATTN_BF16
                              ? launch_fwd_bf16(p, (int)q->d, stream_of(hip_stream))
                              : launch_fwd_f32(p, (int)q->d, stream_of(hip_stream));
     return hip_status(e, "attn_segment_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int seqattn_version(void) { return SEQATTN_VERSION; }
+
+const char *seqattn_status_string(int status)
+{
+    switch (status) {
+    case SEQATTN_OK: return "ok";
+    case SEQATTN_ERR_NULL: return "null pointer";
+    case SEQATTN_ERR_DTYPE: return "unsupported or mismatched dtype";
+    case SEQATTN_ERR_SHAPE: return "invalid shape";
+    case SEQATTN_ERR_STRIDE: return "invalid stride or alignment";
+    case SEQATTN_ERR_ALIAS: return "output aliases an input";
+    case SEQATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SEQATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SEQATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *seqattn_last_error(void) { return g_err; }
+
+int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
+                             const seqattn_tensor *v, int64_t causal_offset,
+                             float softmax_scale, uint32_t flags, seqattn_tensor *o,
+                             seqattn_tensor *lse, void *hip_stream)
+{
+    return segment_fwd(q, k, v, causal_offset, softmax_scale, flags, o, lse, nullptr, 0, false,
+                       hip_stream);
+}
+
+int seqattn_attn_segment_fwd_ws(const seqattn_tensor *q, const seqattn_tensor *k,
+                                const seqattn_tensor *v, int64_t causal_offset,
+                                float softmax_scale, uint32_t flags, seqattn_tensor *o,
+                                seqattn_tensor *lse, void *workspace, size_t workspace_bytes,
+                                void *hip_stream)
+{
+    return segment_fwd(q, k, v, causal_offset, softmax_scale, flags, o, lse, workspace,
+                       workspace_bytes, true, hip_stream);
 }
 
 int seqattn_lse_merge(seqattn_tensor *o_acc, seqattn_tensor *lse_acc,
@@ -427,6 +542,9 @@ size_t seqattn_workspace_size(int op, const seqattn_tensor *q, const seqattn_ten
     if (!q)
         return 0;
     switch (op) {
+    case SEQATTN_OP_SEGMENT_FWD:
+        // fp32 partials of a key-range split (seqattn_attn_segment_fwd_ws)
+        return segment_split_bytes(q, segment_split(q, k));
     case SEQATTN_OP_DILATED_FWD:
         // fp32 accumulator when the output o (passed as `k`) is bf16
         if (k && k->dtype == SEQATTN_BF16)

@@ -32,6 +32,26 @@ struct FwdParams {
     // ceil((hs_len - h mod r) / r) rows; Nq = Nk is the count at offset 0.
     int hs_r = 0, hs_len = 0;
     int grouped = 0;     // work order (work_item): 0 default, else the band
+    // Key-range split (kv_chunk 0: none).  With kv_chunk > 0 (a multiple of
+    // twice the key tile) the launch runs nchunk work items per query tile,
+    // item c taking keys [c kv_chunk, (c + 1) kv_chunk) of the tile's visible
+    // range; o and lse are fp32 partials, chunk c at o + c o_chunk and
+    // lse + c l_chunk elements.  A chunk past the visible range writes nothing.
+    int kv_chunk = 0, nchunk = 1;
+    int64_t o_chunk = 0, l_chunk = 0;
+};
+
+// Merge of the key-range chunks of a split segment forward (FwdParams'
+// kv_chunk) into the call's output: per row, the chunks its query tile
+// computed, combined by their log-sum-exp.
+struct ChunkMergeParams {
+    View o, lse;                 // the call's output
+    const float *po, *pl;        // partials: po[c][B][H][N][d], pl[c][B][H][N]
+    int B, H, N, d, Nk;
+    int delta, noncausal;
+    int tile_rows;               // query rows of the forward's work item
+    int kv_chunk, nchunk;
+    int o_f32;
 };
 
 struct MergeParams {
@@ -139,6 +159,7 @@ struct RelayoutParams {
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t st);
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t st);
+hipError_t launch_chunk_merge(const ChunkMergeParams &p, hipStream_t st);
 // Writes the empty partial (O = 0, LSE = -inf) into an fp32/bf16 o view and lse.
 hipError_t launch_fill_empty(const View &o, const View &lse, int B, int S, int H,
                              int N, int d, int o_f32, hipStream_t st);

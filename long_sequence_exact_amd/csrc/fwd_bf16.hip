@@ -153,7 +153,7 @@ __device__ inline float lane_pair_sum(float x)
 // 64-key tiles, 12 waves, three per SIMD (168 VGPRs); d = 64 with 64-key
 // tiles (at most 128 VGPRs, 32 KiB of LDS), four waves per SIMD: two 8-wave
 // or four 4-wave workgroups per CU.
-template <int D, int BK, int NW = kWaves>
+template <int D, int BK, int NW = kWaves, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd_bf16_kernel(const FwdParams p)
 {
     constexpr int kBQ = 32 * NW;
@@ -172,7 +172,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
 
     const int nqt = (p.Nq + kBQ - 1) / kBQ;
     const int BH = p.B * p.S * p.Hq;
-    const WorkItem wi = work_item(blockIdx.x, nqt, BH, p.grouped);
+    // a split launch runs nchunk items per query tile, chunk index fastest
+    const int chunk = SPLIT ? (int)(blockIdx.x % (unsigned)p.nchunk) : 0;
+    const unsigned item = SPLIT ? blockIdx.x / (unsigned)p.nchunk : blockIdx.x;
+    const WorkItem wi = work_item(item, nqt, BH, p.grouped);
     if (wi.grp >= BH)
         return;  // padding item of a grouped launch
     const int qt = nqt - 1 - wi.t;
@@ -204,6 +207,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
     if (!p.noncausal) {
         const int lim = q0 + kBQ + p.delta;  // keys < lim can be visible
         kv_end = min(kv_end, max(lim, 0));
+    }
+    int t_begin = 0;  // first key tile (even: the buffers alternate from it)
+    if constexpr (SPLIT) {
+        const int jb = chunk * p.kv_chunk;
+        if (jb >= kv_end)
+            return;  // nothing of this chunk is visible: the merge skips it
+        kv_end = min(kv_end, jb + p.kv_chunk);
+        t_begin = jb / BK;
     }
     const int ntiles = (kv_end + BK - 1) / BK;
 
@@ -281,8 +292,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
     for (int i = 0; i < D / 32; ++i)
         vlane[i] = vbase + ((i ^ vsw) << 6);
 
-    if (ntiles > 0)
-        issue_tile(0);
+    if (ntiles > t_begin)
+        issue_tile(t_begin);
 
     // one tile; kbuf and vbuf are the tile's K and V buffers (the loop below
     // runs two tiles per iteration, so both are known addresses and the LDS
@@ -471,7 +482,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
     };
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = t_begin; t < ntiles; t += 2) {
         step(t, lds, lds + 2 * TILEB);
         if (t + 1 < ntiles)
             step(t + 1, lds + TILEB, lds + 3 * TILEB);
@@ -488,8 +499,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
     const int64_t ro = head_shift_elems(p.o, p.hs_r, hr.off);
     const int64_t rl = head_shift_elems(p.lse, p.hs_r, hr.off);
     float *Lp = (float *)p.lse.ptr + b * p.lse.sb + s * p.lse.ss + h * p.lse.sh + rl +
-                (int64_t)qrow * p.lse.sn;
-    const int64_t orow = b * p.o.sb + s * p.o.ss + h * p.o.sh + ro + (int64_t)qrow * p.o.sn;
+                (int64_t)qrow * p.lse.sn + chunk * p.l_chunk;
+    const int64_t orow = b * p.o.sb + s * p.o.ss + h * p.o.sh + ro + (int64_t)qrow * p.o.sn +
+                         chunk * p.o_chunk;
 
     if (!p.accumulate) {
         if (hl == 0)
@@ -555,6 +567,18 @@ hipError_t launch_fwd_bf16(const FwdParams &p0, int d, hipStream_t st)
     int nqt = (p.Nq + kBQ - 1) / kBQ;
     if ((int64_t)nqt * BH == 0)
         return hipSuccess;
+    if (p.kv_chunk > 0) {
+        // a split call (too few query tiles to fill the chip): 8-wave items,
+        // nchunk per query tile, in the default order
+        if (d != 128 || p.accumulate || p.hs_r > 0 || p.kv_chunk % (2 * 128) != 0)
+            return hipErrorInvalidValue;
+        p.grouped = 0;
+        const int64_t grid = work_items(nqt, BH, 0) * p.nchunk;
+        if (!grid_fits(grid, kThreads))
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, 128, kWaves, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+        return hipGetLastError();
+    }
     const int nqt12 = (p.Nq + 383) / 384;
     if (d == 128 && !p.accumulate && p.Nq >= 16384 &&
         (int64_t)nqt12 * BH >= 4 * kXcds * kXcdCUs) {

@@ -80,6 +80,82 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p)
     }
 }
 
+__device__ inline unsigned pack2(float a, float b)
+{
+    bf16 x = (bf16)a, y = (bf16)b;
+    return (unsigned)__builtin_bit_cast(unsigned short, x) |
+           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+// The key-range chunks of a split segment forward merged into its output:
+// for row n, the chunks its query tile computed (those starting below the
+// tile's visible key range, as the forward decides it) are combined by their
+// log-sum-exp; a row with none gets (0, -inf).  One thread per 8 elements of
+// a row, as in lse_merge_kernel.
+__global__ __launch_bounds__(256) void chunk_merge_kernel(const ChunkMergeParams p)
+{
+    const int tpr = p.d / 8;
+    const int64_t total = (int64_t)p.B * p.H * p.N * tpr;
+    const int64_t bhn = (int64_t)p.B * p.H * p.N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total;
+         gid += stride) {
+        const int64_t row = gid / tpr;  // [B][H][N] row of the partials
+        const int c8 = (int)(gid % tpr) * 8;
+        const int n = (int)(row % p.N);
+        const int64_t bh = row / p.N;
+        const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+        int kv_end = p.Nk;
+        if (!p.noncausal) {
+            const int tile = n / p.tile_rows;
+            kv_end = min(kv_end, max((tile + 1) * p.tile_rows + p.delta, 0));
+        }
+        const int nc = min(p.nchunk, (kv_end + p.kv_chunk - 1) / p.kv_chunk);
+        float lc[8];  // static indices only (registers)
+        float M = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            lc[c] = -INFINITY;
+            if (c < nc)
+                lc[c] = p.pl[c * bhn + row];
+            M = fmaxf(M, lc[c]);
+        }
+        float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+        float tot = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (c >= nc)
+                    break;
+                const float w = __expf(lc[c] - M);
+                const float *src = p.po + (c * bhn + row) * p.d + c8;
+                const float4 x0 = *(const float4 *)src, x1 = *(const float4 *)(src + 4);
+                tot += w;
+                a0.x += w * x0.x; a0.y += w * x0.y; a0.z += w * x0.z; a0.w += w * x0.w;
+                a1.x += w * x1.x; a1.y += w * x1.y; a1.z += w * x1.z; a1.w += w * x1.w;
+            }
+            const float inv = 1.f / tot;
+            a0.x *= inv; a0.y *= inv; a0.z *= inv; a0.w *= inv;
+            a1.x *= inv; a1.y *= inv; a1.z *= inv; a1.w *= inv;
+        }
+        const int64_t off = b * p.o.sb + h * p.o.sh + (int64_t)n * p.o.sn + c8;
+        if (p.o_f32) {
+            *(float4 *)((float *)p.o.ptr + off) = a0;
+            *(float4 *)((float *)p.o.ptr + off + 4) = a1;
+        } else {
+            uint4 w;
+            w.x = pack2(a0.x, a0.y);
+            w.y = pack2(a0.z, a0.w);
+            w.z = pack2(a1.x, a1.y);
+            w.w = pack2(a1.z, a1.w);
+            *(uint4 *)((bf16 *)p.o.ptr + off) = w;
+        }
+        if (c8 == 0)
+            *((float *)p.lse.ptr + b * p.lse.sb + h * p.lse.sh + (int64_t)n * p.lse.sn) =
+                M == -INFINITY ? -INFINITY : M + __logf(tot);
+    }
+}
+
 // (O, LSE) <- (0, -inf) over a [B][S][H][N] view
 __global__ __launch_bounds__(256) void fill_empty_kernel(View o, View lse, int B, int S,
                                                          int H, int N, int d, int o_f32)
@@ -108,13 +184,6 @@ __global__ __launch_bounds__(256) void fill_empty_kernel(View o, View lse, int B
             *((float *)lse.ptr + b * lse.sb + s * lse.ss + h * lse.sh + (int64_t)n * lse.sn) =
                 -INFINITY;
     }
-}
-
-__device__ inline unsigned pack2(float a, float b)
-{
-    bf16 x = (bf16)a, y = (bf16)b;
-    return (unsigned)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
 }
 
 __global__ __launch_bounds__(256) void cast_bf16_kernel(View src, View dst, int B, int H,
@@ -156,6 +225,17 @@ hipError_t launch_lse_merge(const MergeParams &p, hipStream_t st)
     if (threads == 0)
         return hipSuccess;
     hipLaunchKernelGGL(lse_merge_kernel, dim3(grid_for(threads)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_merge(const ChunkMergeParams &p, hipStream_t st)
+{
+    const int64_t threads = (int64_t)p.B * p.H * p.N * (p.d / 8);
+    if (threads == 0)
+        return hipSuccess;
+    if (p.nchunk < 1 || p.nchunk > 8 || p.d % 8 != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(chunk_merge_kernel, dim3(grid_for(threads)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

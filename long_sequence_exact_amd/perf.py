@@ -22,6 +22,10 @@ the launch stream, inputs already resident in HBM:
                       (fp32 accumulator + bf16 partial), reported in GB/s
   ulysses_len_sweep   the 128K call's shape (4 heads, d = 128, causal, one
                       launch) at 16K, 32K, 64K, 128K and 256K tokens
+  short_calls         d = 128 calls with fewer 256-row query tiles than
+                      compute units, with the key-range split (default) and
+                      without it (split=False): 4 heads causal at 2K, 4K, 8K;
+                      1 head causal at 32K; 1 head non-causal at 16K
 FLOPs are algorithmic (4*d per visible pair forward, 10*d backward); bytes
 for the merge are the tensors read and written.  The ring lines also time
 every (rank, step) call alone, as on a device of its own, and report the
@@ -237,6 +241,26 @@ def run(name, reps):
             res[f"{n // 1024}k_TFLOP/s"] = round(fl_n / ms_n / 1e9, 1)
             del q, k, v, out, lse
         return res
+    elif name == "short_calls":
+        res = {"workload": name}
+        for tag, hq, n, delta in (("4h_2k", 4, 2048, 0), ("4h_4k", 4, 4096, 0),
+                                  ("4h_8k", 4, 8192, 0), ("1h_32k", 1, 32768, 0),
+                                  ("1h_16k_noncausal", 1, 16384, None)):
+            q, k, v = draw([(1, hq, n, 128)] * 3, 20 + n // 1024 + hq, torch.bfloat16)
+            q, k, v = q.to(dev), k.to(dev), v.to(dev)
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+            ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+            fl_n = 4.0 * 128 * hq * pairs(n, n, delta)
+            for sp in (True, False):
+                ms_n = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=delta, out=out,
+                                                      lse=lse, workspace=ws, split=sp),
+                             max(4, reps * 4))
+                key = tag if sp else tag + "_unsplit"
+                res[f"{key}_ms"] = round(ms_n, 4)
+                res[f"{key}_TFLOP/s"] = round(fl_n / ms_n / 1e9, 1)
+            del q, k, v, out, lse, ws
+        return res
     elif name == "longnet_32k_bf16":
         q, k, v, do = (t.to(dev) for t in workload_inputs(w, with_dout=True))
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
@@ -335,7 +359,7 @@ def main():
                     default=["ulysses_128k_bf16", "ring_16k_bf16", "ring_16k_bf16_zigzag",
                              "longnet_32k_bf16", "longnet_page_32k_bf16",
                              "usp_gqa_256k_bf16", "ulysses_relayout", "lse_merge",
-                             "ulysses_len_sweep"])
+                             "ulysses_len_sweep", "short_calls"])
     ap.add_argument("--reps", type=int, default=10)
     args = ap.parse_args()
     print(json.dumps({"kernel_sources_sha256_16": source_hashes(),

@@ -378,3 +378,53 @@ def test_plain_c_caller(L, tmp_path):
     assert lines["null"].split(" | ")[1]          # the detail message is set
     assert lines["shape"].startswith(f"{ESHAPE} ")
     assert lines["alias"].startswith(f"{EALIAS} ")
+
+
+def test_split_forward_workspace(L):
+    """seqattn_attn_segment_fwd_ws: the workspace size follows the split rule
+    (bf16, d = 128, at least 1024 keys, fewer 256-row tiles than the GPU's
+    256 compute units, chunks of at least 512 keys aiming at one work item
+    per compute unit), and a split call without enough aligned,
+    non-overlapping workspace is refused before any HIP call."""
+    r = ctypes.byref
+    step = 1 << 30
+
+    def size(hq, nq, nk, d=128, dt=_lib.BF16):
+        qq = T(BASE, dt, 1, hq, nq, d)
+        kk = T(BASE + step, dt, 1, 1, nk, d)
+        return L.seqattn_workspace_size(_lib.OP_SEGMENT_FWD, r(qq), r(kk), 0)
+
+    def chunks(hq, nq, nk):
+        per = hq * nq * (128 + 1) * 4  # fp32 O and LSE of every row
+        assert size(hq, nq, nk) % per == 0
+        return size(hq, nq, nk) // per
+
+    assert chunks(2, 16384, 16384) == 2    # 128 tiles: two chunks of 8192 keys
+    assert chunks(4, 4096, 4096) == 4      # 64 tiles: four of 1024
+    assert chunks(4, 2048, 2048) == 4      # 32 tiles: eight wanted, 512 keys at least
+    assert chunks(1, 1000, 9000) == 8      # 4 tiles: at most eight (1280 keys)
+    assert chunks(3, 5000, 9000) == 5      # 60 tiles, ragged: five wanted, 2048 keys
+    assert size(4, 16384, 16384) == 0      # 256 tiles fill the chip
+    assert size(2, 16384, 1023) == 0       # too few keys
+    assert size(2, 16384, 16384, dt=_lib.F32) == 0
+    assert size(2, 16384, 16384, d=64) == 0
+    # 2 heads x 16384 rows, split in two
+    q = T(BASE, _lib.BF16, 1, 2, 16384, 128)
+    k = T(BASE + step, _lib.BF16, 1, 2, 16384, 128)
+    v = T(BASE + 2 * step, _lib.BF16, 1, 2, 16384, 128)
+    o = T(BASE + 3 * step, _lib.BF16, 1, 2, 16384, 128)
+    lse = LSE(BASE + 4 * step, 1, 2, 16384)
+    need = L.seqattn_workspace_size(_lib.OP_SEGMENT_FWD, r(q), r(k), 0)
+    assert need == 2 * (2 * 16384) * (128 + 1) * 4
+    ws = BASE + 5 * step
+
+    def call(ws_=ws, wsb=need, flags=0, o_=o):
+        return L.seqattn_attn_segment_fwd_ws(r(q), r(k), r(v), 0, 0.0, flags, r(o_), r(lse),
+                                             ws_, wsb, None)
+
+    assert call(ws_=None, wsb=0) == EWS
+    assert call(wsb=need - 4) == EWS
+    assert call(ws_=ws + 4) == EWS                     # misaligned
+    assert call(ws_=BASE + 2 * step + 4096) == EALIAS  # inside v
+    # an accumulating call is not split (and checks its output dtype first)
+    assert call(ws_=None, wsb=0, flags=1) == EDTYPE

@@ -14,7 +14,7 @@ import long_sequence_exact_amd as sa
 from long_sequence_exact_amd import emulate
 from long_sequence_exact_amd.synth import (WORKLOADS, draw, sample_rows, sample_rows_per_tile,
                                            workload_inputs)
-from tests.parity import LSE_TOL, TOL, assert_parity, to_np
+from tests.parity import LSE_TOL, TOL, assert_parity, check_close, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -407,6 +407,59 @@ def test_long_call_shape(hq, hkv, nq, nk, delta, odt):
         assert (out.cpu()[0][:, empty] == 0).all()
     assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // nq,
                   what=f"long call {nq}x{nk}")
+
+
+SPLIT_CASES = [
+    # (hq, hkv, nq, nk, delta, out dtype): calls with fewer 256-row tiles than
+    # compute units and at least 1024 keys, whose key ranges are split
+    (2, 2, 16384, 16384, 0, torch.bfloat16),       # 2 chunks of 8192 keys
+    (2, 1, 8000, 12000, 4000, torch.float32),      # ragged, keys ahead: 4 of 3072
+    (3, 1, 5000, 9000, None, torch.bfloat16),      # non-causal: 5 of 2048
+    (2, 1, 16384, 16384, -3000, torch.float32),    # early rows see no key
+    (4, 4, 2048, 2048, 0, torch.bfloat16),         # 4 chunks of 512
+    (1, 1, 1000, 9000, 8500, torch.bfloat16),      # 8 chunks of 1280
+]
+
+
+@pytest.mark.parametrize("hq,hkv,nq,nk,delta,odt", SPLIT_CASES)
+def test_split_short_call(hq, hkv, nq, nk, delta, odt):
+    """Short calls split their key ranges over more workgroups and merge the
+    fp32 partials by LSE.  O and LSE start as NaN; every O row must come
+    back finite and every LSE row finite or -inf exactly where the oracle
+    says the row sees no key; one seeded row in every 32-row slice of every
+    head against the oracle, and every row against the unsplit call."""
+    d = 128
+    q, k, v = draw([(1, hq, nq, d), (1, hkv, nk, d), (1, hkv, nk, d)], 1600 + nq + hq)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    outs = []
+    for split in (True, False):
+        out = torch.full(q.shape, float("nan"), dtype=odt, device=DEV)
+        lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device=DEV)
+        sa.attn_segment_fwd(qd, kd, vd, causal_offset=delta, out=out, lse=lse, split=split)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    (out, lse), (out1, lse1) = outs
+    assert torch.isfinite(out).all(), "unwritten or non-finite O rows"
+    assert not torch.isnan(lse).any(), "unwritten LSE rows"
+    rows = []
+    for h in range(hq):
+        rows += [h * nq + i for i in sample_rows_per_tile(nq, 32, 1, 1700 + h, must=(0, nq - 1))]
+    rows = np.array(rows, np.int64)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v), delta=_delta_arg(delta),
+                                   rows=rows)
+    og = to_np(out).reshape(-1, d)[rows]
+    lg = to_np(lse).reshape(-1)[rows]
+    if delta is not None and delta < 0:
+        empty = torch.arange(nq) + delta < 0
+        assert torch.isneginf(lse.cpu()[0][:, empty]).all()
+        assert (out.cpu()[0][:, empty] == 0).all()
+    assert_parity(og, lg, o_ref, l_ref, torch.bfloat16, rows_heads=rows // nq,
+                  what=f"split call {nq}x{nk}")
+    # every row against the unsplit call (same inputs, other merge order)
+    assert torch.equal(torch.isneginf(lse), torch.isneginf(lse1))
+    fin = torch.isfinite(lse1)
+    assert (lse[fin] - lse1[fin]).abs().max().item() <= LSE_TOL
+    check_close(out, to_np(out1), TOL[torch.bfloat16], what="split vs unsplit", name="o")
 
 
 def test_usp_forward_full_size_sampled():
