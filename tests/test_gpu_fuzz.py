@@ -1,6 +1,7 @@
 """Seeded random sweep against the fp64 oracle: shapes, causal offsets, head
 groupings, layouts and flags drawn by one generator, for the segment forward
-(bf16 and fp32, with and without the fused merge), its backward and dilated
+(bf16 and fp32, with and without the fused merge; short d = 128 calls with
+and without the key-range split), its backward and dilated
 attention (forward and backward, with and without head-dependent offsets),
 batch 1 or 2.
 
@@ -18,7 +19,7 @@ import torch
 import oracle
 import long_sequence_exact_amd as sa
 from long_sequence_exact_amd.synth import draw
-from tests.parity import TOL, assert_parity, check_close, to_np
+from tests.parity import LSE_TOL, TOL, assert_parity, check_close, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -80,6 +81,49 @@ def test_fuzz_segment_fwd(case):
                                    out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
     torch.cuda.synchronize()
     assert_parity(to_np(o), to_np(l), o_ref, l_ref, dtype, what=what)
+
+
+def _split_cases(count, seed):
+    """d = 128 bf16 calls short enough for the key-range split (fewer 256-row
+    query tiles than compute units, at least 1024 keys)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        hkv = int(rng.integers(1, 3))
+        group = int(rng.choice([1, 2, 4]))
+        nq = int(rng.integers(1, 1200))
+        nk = int(rng.integers(1024, 4097))
+        delta = None if rng.random() < 0.25 else int(rng.integers(-nq - 50, nk + 50))
+        out_bf16 = bool(rng.random() < 0.5)
+        seq_major = bool(rng.random() < 0.3)
+        bsz = 2 if rng.random() < 0.25 else 1
+        out.append((i, hkv, group, nq, nk, delta, out_bf16, seq_major, bsz))
+    return out
+
+
+@pytest.mark.parametrize("case", _split_cases(12 * SCALE, 20261204), ids=lambda c: f"split{c[0]}")
+def test_fuzz_split_fwd(case):
+    """The split call against the oracle on every row, and against the
+    unsplit call (same -inf rows, LSE within its tolerance, O by the per-row
+    measure)."""
+    i, hkv, group, nq, nk, delta, out_bf16, seq_major, bsz = case
+    hq, d = hkv * group, 128
+    q, k, v = draw([(bsz, hq, nq, d), (bsz, hkv, nk, d), (bsz, hkv, nk, d)], 7500 + i)
+    o_ref, l_ref = oracle.attn_fwd(_np32(q), _np32(k), _np32(v),
+                                   delta=oracle.NONCAUSAL if delta is None else delta)
+    qd, kd, vd = (_dev(t, seq_major) for t in (q, k, v))
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    res = [sa.attn_segment_fwd(qd, kd, vd, causal_offset=delta, out_dtype=odt, split=sp)
+           for sp in (True, False)]
+    torch.cuda.synchronize()
+    (o, l), (o1, l1) = res
+    what = f"case {case}"
+    assert_parity(to_np(o), to_np(l), o_ref, l_ref, torch.bfloat16, what=what)
+    assert torch.equal(torch.isneginf(l), torch.isneginf(l1)), what
+    fin = torch.isfinite(l1)
+    if fin.any():
+        assert (l[fin] - l1[fin]).abs().max().item() <= LSE_TOL, what
+    check_close(o, to_np(o1), TOL[torch.bfloat16], what=what + " split vs unsplit", name="o")
 
 
 def _bwd_cases(count, seed):
