@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SEQATTN_VERSION 100 /* 1.0.0 */
+#define SEQATTN_VERSION 110 /* 1.1.0: adds seqattn_attn_segment_fwd_ws */
 
 typedef enum {
     SEQATTN_OK = 0,

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (seqattn_\w+)", out))
     assert set(declared_functions()) <= exported
-    assert L.seqattn_version() == 100
+    assert L.seqattn_version() == 110
 
 
 BASE = 0x7f0000000000  # fake, 256-byte aligned device addresses (never touched)
@@ -373,7 +373,7 @@ def test_plain_c_caller(L, tmp_path):
     f = _lib.Tensor
     assert lines["size"] == (f"{ctypes.sizeof(f)} data {f.data.offset} dtype {f.dtype.offset} "
                              f"b {f.b.offset} d {f.d.offset} stride_n {f.stride_n.offset}")
-    assert lines["version"] == "100"
+    assert lines["version"] == "110"
     assert lines["null"].startswith(f"{ENULL} ")
     assert lines["null"].split(" | ")[1]          # the detail message is set
     assert lines["shape"].startswith(f"{ESHAPE} ")
