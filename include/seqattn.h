@@ -124,12 +124,12 @@ int seqattn_attn_segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k,
 
 /*
  * seqattn_attn_segment_fwd_ws -- seqattn_attn_segment_fwd with a caller-owned
- * workspace, for calls too short to fill the GPU: when the query block's
- * 256-row tiles are fewer than the GPU's 256 compute units (bf16, d = 128, at
- * least 1024 keys, no SEQATTN_ACCUMULATE), each tile's keys are cut into 2-8
- * chunks of at least 512 keys (about one work item per compute unit in all)
- * computed by separate workgroups, whose fp32 partials (O, LSE) go to
- * the workspace and are then merged by their log-sum-exp into o and lse
+ * workspace, for calls too short to fill the GPU (bf16, d = 128, at least
+ * 1024 keys, no SEQATTN_ACCUMULATE): when the query block's 256-row tiles
+ * are fewer than two per compute unit (causal) or than one (non-causal),
+ * each tile's visible keys are cut into 2-8 equal parts (at least 512
+ * keys), computed by separate workgroups, whose fp32 partials (O, LSE) go
+ * to the workspace and are then merged by their log-sum-exp into o and lse
  * ("Ultra-Long Sequence Distributed Transformer", Abstract: partial
  * attention per segment, combined exactly).  The result equals the unsplit
  * call's up to rounding order; a call the rule does not split runs exactly

@@ -312,32 +312,37 @@ std::vector<HeadSel> head_sels(bool shift, int64_t r, int Hq, int Hkv, bool kern
 }
 
 // Key-range split of a segment forward whose 256-row query tiles are too
-// few to fill the chip (fewer than its compute units): each tile's keys are
-// cut into nchunk chunks of kv_chunk keys, computed by separate workgroups
-// into fp32 partials and merged by their LSE.  Decided from the shapes alone
-// (bf16, d = 128): about one work item per compute unit, chunks of at least
-// 512 keys.  Fewer, longer chunks beat more items: at 8K tokens and 4 heads
-// two chunks per tile ran 0.112 ms, four 0.127, none 0.167.
+// few to fill the chip: each tile's visible keys are cut into nchunk equal
+// parts (at least kv_chunk = 512 keys), computed by separate workgroups into
+// fp32 partials and merged by their LSE.  A non-causal call with fewer tiles
+// than compute units aims at one item per CU (all items equal).  A causal
+// call with fewer than two tiles per CU aims at two items per CU: the parts
+// shrink with their tiles, and heavy-first dispatch gives each CU one long
+// and one short item (4 heads at 16K: 0.349 ms unsplit).  Decided from the
+// shapes and causality alone (bf16, d = 128); the causal rule, which never
+// takes fewer chunks, sizes the workspace.  Parts of at least 512 keys beat
+// longer ones on the light tiles (8K tokens, 4 heads: 0.096 against 0.103 ms
+// with 1024).
 struct SegmentSplit {
     int nchunk = 1, kv_chunk = 0;
 };
 
-SegmentSplit segment_split(const seqattn_tensor *q, const seqattn_tensor *k)
+SegmentSplit segment_split(const seqattn_tensor *q, const seqattn_tensor *k, bool causal)
 {
-    constexpr int64_t kTarget = 256;     // work items per launch aimed at (one per CU)
-    constexpr int64_t kMinChunk = 512;   // keys per chunk, at least
+    constexpr int64_t kMinChunk = 512;
     SegmentSplit sp;
     if (!q || !k || q->dtype != SEQATTN_BF16 || q->d != 128 || k->n < 2 * kMinChunk)
         return sp;
     const int64_t tiles = q->b * q->h * ((q->n + 255) / 256);
-    if (tiles == 0 || tiles >= kSplitCUs)
+    const int64_t items = causal ? 2 * kSplitCUs : kSplitCUs;
+    if (tiles == 0 || tiles >= items)
         return sp;
-    const int64_t want = std::min<int64_t>((kTarget + tiles - 1) / tiles, 8);
-    // chunks a multiple of 256 keys (two key tiles)
-    int64_t chunk = (k->n + want - 1) / want;
-    chunk = std::max((chunk + 255) / 256 * 256, kMinChunk);
-    sp.kv_chunk = (int)chunk;
-    sp.nchunk = (int)((k->n + chunk - 1) / chunk);
+    const int64_t want = std::min<int64_t>((items + tiles - 1) / tiles, 8);
+    // the longest tile's parts: at least 1024 keys from 4096 keys on (eight
+    // parts of 512 at 4K tokens and 4 heads took 0.057 ms, four 0.044)
+    const int64_t cap = k->n / (k->n >= 4096 ? 1024 : kMinChunk);
+    sp.nchunk = (int)std::min<int64_t>(want, cap);
+    sp.kv_chunk = (int)kMinChunk;
     if (sp.nchunk < 2)
         sp = SegmentSplit();
     return sp;
@@ -393,7 +398,8 @@ int segment_fwd(const seqattn_tensor *q, const seqattn_tensor *k, const seqattn_
                                             p.o_f32, stream_of(hip_stream)),
                           "fill_empty");
     }
-    const SegmentSplit sp = may_split && !acc ? segment_split(q, k) : SegmentSplit();
+    const SegmentSplit sp =
+        may_split && !acc ? segment_split(q, k, !p.noncausal) : SegmentSplit();
     if (sp.nchunk > 1) {
         const size_t need = segment_split_bytes(q, sp);
         if (!workspace || workspace_bytes < need)
@@ -544,7 +550,7 @@ size_t seqattn_workspace_size(int op, const seqattn_tensor *q, const seqattn_ten
     switch (op) {
     case SEQATTN_OP_SEGMENT_FWD:
         // fp32 partials of a key-range split (seqattn_attn_segment_fwd_ws)
-        return segment_split_bytes(q, segment_split(q, k));
+        return segment_split_bytes(q, segment_split(q, k, true));
     case SEQATTN_OP_DILATED_FWD:
         // fp32 accumulator when the output o (passed as `k`) is bf16
         if (k && k->dtype == SEQATTN_BF16)

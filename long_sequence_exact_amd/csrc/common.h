@@ -33,10 +33,11 @@ struct FwdParams {
     int hs_r = 0, hs_len = 0;
     int grouped = 0;     // work order (work_item): 0 default, else the band
     // Key-range split (kv_chunk 0: none).  With kv_chunk > 0 (a multiple of
-    // twice the key tile) the launch runs nchunk work items per query tile,
-    // item c taking keys [c kv_chunk, (c + 1) kv_chunk) of the tile's visible
-    // range; o and lse are fp32 partials, chunk c at o + c o_chunk and
-    // lse + c l_chunk elements.  A chunk past the visible range writes nothing.
+    // 256) the launch runs nchunk work items per query tile: the tile's
+    // visible keys [0, e) are cut into parts of len = max(kv_chunk, e / nchunk
+    // rounded up to 256) keys, item c taking [c len, (c + 1) len); o and lse
+    // are fp32 partials, chunk c at o + c o_chunk and lse + c l_chunk
+    // elements.  A chunk past the visible range writes nothing.
     int kv_chunk = 0, nchunk = 1;
     int64_t o_chunk = 0, l_chunk = 0;
 };

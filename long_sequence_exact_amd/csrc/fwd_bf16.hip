@@ -210,10 +210,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : (BK == 64 ? 3 : 2)) void fwd
     }
     int t_begin = 0;  // first key tile (even: the buffers alternate from it)
     if constexpr (SPLIT) {
-        const int jb = chunk * p.kv_chunk;
+        // this tile's visible keys in nchunk equal parts (whole 256-key
+        // steps, at least kv_chunk keys), so a causal launch's items shrink
+        // with their tiles and heavy-first dispatch pairs long with short
+        const int len = max(p.kv_chunk, ((kv_end + p.nchunk - 1) / p.nchunk + 255) / 256 * 256);
+        const int jb = chunk * len;
         if (jb >= kv_end)
             return;  // nothing of this chunk is visible: the merge skips it
-        kv_end = min(kv_end, jb + p.kv_chunk);
+        kv_end = min(kv_end, jb + len);
         t_begin = jb / BK;
     }
     const int ntiles = (kv_end + BK - 1) / BK;

@@ -88,8 +88,8 @@ __device__ inline unsigned pack2(float a, float b)
 }
 
 // The key-range chunks of a split segment forward merged into its output:
-// for row n, the chunks its query tile computed (those starting below the
-// tile's visible key range, as the forward decides it) are combined by their
+// for row n, the chunks its query tile computed (the parts of the tile's
+// visible key range, as the forward cuts it) are combined by their
 // log-sum-exp; a row with none gets (0, -inf).  One thread per 8 elements of
 // a row, as in lse_merge_kernel.
 __global__ __launch_bounds__(256) void chunk_merge_kernel(const ChunkMergeParams p)
@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(const ChunkMergeParams
             const int tile = n / p.tile_rows;
             kv_end = min(kv_end, max((tile + 1) * p.tile_rows + p.delta, 0));
         }
-        const int nc = min(p.nchunk, (kv_end + p.kv_chunk - 1) / p.kv_chunk);
+        // the forward's parts of this tile's visible keys (same rule)
+        const int len = max(p.kv_chunk, ((kv_end + p.nchunk - 1) / p.nchunk + 255) / 256 * 256);
+        const int nc = min(p.nchunk, (kv_end + len - 1) / len);
         float lc[8];  // static indices only (registers)
         float M = -INFINITY;
 #pragma unroll

@@ -250,7 +250,7 @@ def run(name, reps):
             q, k, v = q.to(dev), k.to(dev), v.to(dev)
             out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
             lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-            ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+            ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
             fl_n = 4.0 * 128 * hq * pairs(n, n, delta)
             for sp in (True, False):
                 ms_n = timed(lambda: attn_segment_fwd(q, k, v, causal_offset=delta, out=out,

@@ -382,10 +382,11 @@ def test_plain_c_caller(L, tmp_path):
 
 def test_split_forward_workspace(L):
     """seqattn_attn_segment_fwd_ws: the workspace size follows the split rule
-    (bf16, d = 128, at least 1024 keys, fewer 256-row tiles than the GPU's
-    256 compute units, chunks of at least 512 keys aiming at one work item
-    per compute unit), and a split call without enough aligned,
-    non-overlapping workspace is refused before any HIP call."""
+    for a causal call, which never takes fewer chunks than a non-causal one
+    (bf16, d = 128, at least 1024 keys, fewer 256-row tiles than two per
+    compute unit, about two items per CU, at most eight chunks, the longest
+    tile's at least 1024 keys from 4096 keys on, else 512), and a split call without enough aligned, non-overlapping
+    workspace is refused before any HIP call."""
     r = ctypes.byref
     step = 1 << 30
 
@@ -399,23 +400,24 @@ def test_split_forward_workspace(L):
         assert size(hq, nq, nk) % per == 0
         return size(hq, nq, nk) // per
 
-    assert chunks(2, 16384, 16384) == 2    # 128 tiles: two chunks of 8192 keys
-    assert chunks(4, 4096, 4096) == 4      # 64 tiles: four of 1024
-    assert chunks(4, 2048, 2048) == 4      # 32 tiles: eight wanted, 512 keys at least
-    assert chunks(1, 1000, 9000) == 8      # 4 tiles: at most eight (1280 keys)
-    assert chunks(3, 5000, 9000) == 5      # 60 tiles, ragged: five wanted, 2048 keys
-    assert size(4, 16384, 16384) == 0      # 256 tiles fill the chip
+    assert chunks(4, 16384, 16384) == 2    # 256 tiles: two items per CU
+    assert chunks(2, 16384, 16384) == 4    # 128 tiles
+    assert chunks(4, 4096, 4096) == 4      # 64 tiles: parts of 1024 from 4096 keys on
+    assert chunks(4, 2048, 2048) == 4      # 32 tiles: at most 2048 / 512 chunks
+    assert chunks(1, 1000, 9000) == 8      # 4 tiles: at most eight
+    assert chunks(3, 5000, 9000) == 8      # 60 tiles, ragged
+    assert size(8, 16384, 16384) == 0      # 512 tiles fill the chip twice
     assert size(2, 16384, 1023) == 0       # too few keys
     assert size(2, 16384, 16384, dt=_lib.F32) == 0
     assert size(2, 16384, 16384, d=64) == 0
-    # 2 heads x 16384 rows, split in two
+    # 2 heads x 16384 rows, split in four
     q = T(BASE, _lib.BF16, 1, 2, 16384, 128)
     k = T(BASE + step, _lib.BF16, 1, 2, 16384, 128)
     v = T(BASE + 2 * step, _lib.BF16, 1, 2, 16384, 128)
     o = T(BASE + 3 * step, _lib.BF16, 1, 2, 16384, 128)
     lse = LSE(BASE + 4 * step, 1, 2, 16384)
     need = L.seqattn_workspace_size(_lib.OP_SEGMENT_FWD, r(q), r(k), 0)
-    assert need == 2 * (2 * 16384) * (128 + 1) * 4
+    assert need == 4 * (2 * 16384) * (128 + 1) * 4
     ws = BASE + 5 * step
 
     def call(ws_=ws, wsb=need, flags=0, o_=o):

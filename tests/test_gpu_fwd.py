@@ -410,14 +410,16 @@ def test_long_call_shape(hq, hkv, nq, nk, delta, odt):
 
 
 SPLIT_CASES = [
-    # (hq, hkv, nq, nk, delta, out dtype): calls with fewer 256-row tiles than
-    # compute units and at least 1024 keys, whose key ranges are split
-    (2, 2, 16384, 16384, 0, torch.bfloat16),       # 2 chunks of 8192 keys
-    (2, 1, 8000, 12000, 4000, torch.float32),      # ragged, keys ahead: 4 of 3072
-    (3, 1, 5000, 9000, None, torch.bfloat16),      # non-causal: 5 of 2048
+    # (hq, hkv, nq, nk, delta, out dtype): short calls (fewer 256-row tiles
+    # than two per compute unit, causal, or than one, non-causal; at least
+    # 1024 keys) whose tiles' visible keys are cut into 2-8 parts
+    (4, 4, 16384, 16384, 0, torch.bfloat16),       # 256 tiles, halves
+    (2, 2, 16384, 16384, 0, torch.bfloat16),       # quarters
+    (2, 1, 8000, 12000, 4000, torch.float32),      # ragged, keys ahead
+    (3, 1, 5000, 9000, None, torch.bfloat16),      # non-causal
     (2, 1, 16384, 16384, -3000, torch.float32),    # early rows see no key
-    (4, 4, 2048, 2048, 0, torch.bfloat16),         # 4 chunks of 512
-    (1, 1, 1000, 9000, 8500, torch.bfloat16),      # 8 chunks of 1280
+    (4, 4, 2048, 2048, 0, torch.bfloat16),         # parts of at least 512 keys
+    (1, 1, 1000, 9000, 8500, torch.bfloat16),      # eight parts
 ]
 
 
